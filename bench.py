@@ -1,0 +1,310 @@
+"""Benchmark: MoE expert-parallel dispatch + combine on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload 2] [--gpus 1]
+
+One step is the whole hot path over one batch of resident synthetic input:
+ep_plan (split counts, scans, exchange plan, stable positions) -> ep_dispatch
+(scatter into the expert-grouped expandX buffer; per-token fp8 for the fp8
+workload) -> ep_combine (weighted gather of the K expert rows per token).
+The uneven all-to-all workload times ep_plan_splits -> ep_dispatch_splits.
+
+Prints one JSON line: whole-job tokens/s, the step's algorithmic HBM GB/s,
+a roofline record for the dominant kernel (its algorithmic bytes per launch
+over its average launch time, HIP events on the launch stream) and the CPU
+oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
+METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4],
+                    help="index of the workload (2: T=8192 H=7168 E=256 K=8 W=16 Zipf)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-reps", type=int, default=5)
+    return ap.parse_args()
+
+
+# --------------------------------------------------------------------------- MoE
+
+class MoEBench:
+    def __init__(self, cfg, torch, ep, workloads):
+        self.cfg, self.torch, self.ep = cfg, torch, ep
+        log(f"[bench] generating inputs for {cfg.name}")
+        inp = workloads.moe_inputs(cfg)
+        self.inp = inp
+        dev = "cuda"
+        t = torch
+        self.ids = t.from_numpy(inp.ids).to(dev)
+        self.x = t.from_numpy(inp.x.view(np.int16)).to(dev)
+        self.w = t.from_numpy(inp.weights).to(dev)
+        self.active = None if inp.active is None else t.from_numpy(inp.active).to(dev)
+        self.ws = ep.alloc_workspace(cfg.T, cfg.K, cfg.E, cfg.W)
+        self.plan = ep.alloc_plan(cfg.T, cfg.K, cfg.E, cfg.W)
+        cap = cfg.cap_rows
+        if cfg.fp8:
+            self.ex = t.empty((cap, cfg.H), dtype=t.uint8, device=dev)
+            self.scales = t.empty(cap, dtype=t.float32, device=dev)
+            # bf16 expert outputs in expandX layout: what the combine reads back
+            g = t.Generator(device=dev)
+            g.manual_seed(cfg.seed + 1000)
+            self.y = t.empty((cap, cfg.H), dtype=t.bfloat16, device=dev)
+            for r0 in range(0, cap, 8192):
+                self.y[r0:r0 + 8192].normal_(generator=g)
+            self.y = self.y.view(t.int16)
+        else:
+            self.ex = t.empty((cap, cfg.H), dtype=t.int16, device=dev)
+            self.scales = None
+            self.y = self.ex          # identity expert: combine reads the dispatched rows
+        self.out = t.empty((cfg.T, cfg.H), dtype=t.int16, device=dev)
+        self.out_dtype = ep.EP_FP8_E4M3FN if cfg.fp8 else ep.EP_BF16
+        # sizes for the byte accounting
+        live_tok = cfg.T if inp.active is None else int(inp.active.sum())
+        self.live_tokens = live_tok
+
+    def plan_step(self):
+        self.ep.ep_plan(self.ids, self.cfg.E, self.cfg.W, self.plan, self.ws, self.active)
+
+    def dispatch_step(self):
+        self.ep.ep_dispatch(self.x, self.plan.pos, self.ex, self.scales, out_dtype=self.out_dtype)
+
+    def combine_step(self):
+        self.ep.ep_combine(self.y, self.plan.pos, self.w, self.out)
+
+    def phases(self):
+        return [("ep_plan", self.plan_step), ("ep_dispatch", self.dispatch_step),
+                ("ep_combine", self.combine_step)]
+
+    def n_rows(self):
+        return int(self.plan.rank_offsets[-1].item())
+
+    def bytes_per_phase(self, N):
+        """Algorithmic HBM bytes: what the method must read and write once."""
+        c = self.cfg
+        tk = c.T * c.K
+        mask_b = 0 if self.inp.active is None else c.T
+        plan_b = tk * 4 + mask_b + tk * 4 + tk * 4          # ids in; pos, occ out
+        row_in = 2 * c.H
+        row_out = c.H if c.fp8 else 2 * c.H
+        disp_b = self.live_tokens * row_in + N * row_out + tk * 4 + (N * 4 if c.fp8 else 0)
+        comb_b = N * 2 * c.H + c.T * 2 * c.H + tk * 4 * 2    # rows in, out rows, pos + weights
+        return {"ep_plan": plan_b, "ep_dispatch": disp_b, "ep_combine": comb_b}
+
+    def tokens(self):
+        return self.cfg.T
+
+    def config_record(self):
+        c = self.cfg
+        return {"workload": c.name, "T": c.T, "H": c.H, "E": c.E, "K": c.K, "W": c.W,
+                "routing": c.routing + (f"(s={c.zipf_s}, {c.n_empty} empty experts)"
+                                        if c.routing == "zipf" else ""),
+                "sigma": c.sigma, "mask_frac": c.mask_frac,
+                "dispatch_rows": "fp8_e4m3fn+fp32 scale" if c.fp8 else "bf16",
+                "combine_rows": "bf16", "accumulate": "fp32"}
+
+    def dtype(self):
+        return "fp8e4m3+bf16" if self.cfg.fp8 else "bf16"
+
+    def cpu_baseline(self, reps):
+        """The serial C oracle on the host: the whole plan, then dispatch and
+        combine of a bounded sample of tokens (all of them for bf16 rows; the
+        first 2048 for fp8 rows, whose definitional encoder is slow), scaled
+        to tokens/s."""
+        import oracle
+        c, inp = self.cfg, self.inp
+        nt = c.T if not c.fp8 else min(c.T, 2048)
+        p0 = oracle.plan(inp.ids, c.E, c.W, inp.active)
+        sub = p0.pos[:nt].copy()
+        live = sub >= 0
+        sub[live] = np.arange(int(live.sum()), dtype=np.int32)   # the sample's rows, compacted
+        m = int(live.sum())
+        yrows = workloads_expert_rows(m, c.H, c.seed) if c.fp8 else None
+        xs, ws = np.ascontiguousarray(inp.x[:nt]), np.ascontiguousarray(inp.weights[:nt])
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            p = oracle.plan(inp.ids, c.E, c.W, inp.active)
+            t1 = time.perf_counter()
+            if c.fp8:
+                q, sc = oracle.dispatch_fp8(xs, sub, m)
+                out = oracle.combine(yrows, sub, ws)
+                del q, sc, out
+            else:
+                ex = oracle.dispatch_bf16(xs, sub, m)
+                out = oracle.combine(ex, sub, ws)
+                del ex, out
+            t2 = time.perf_counter()
+            times.append((t1 - t0) + (t2 - t1) * c.T / nt)
+            del p
+        sec = float(np.median(times))
+        return {"value": c.T / sec, "unit": "tokens/s", "cores": 1, "kind": "oracle",
+                "sample": f"plan of all {c.T} tokens + dispatch/combine of {nt} tokens "
+                          f"(scaled to {c.T}); serial C oracle, one host thread, median of {reps}",
+                "seconds_per_step": sec}
+
+
+def workloads_expert_rows(n, H, seed):
+    import workloads
+    return workloads.expert_outputs(n, H, seed)
+
+
+# --------------------------------------------------------------------------- 1-D
+
+class SplitsBench:
+    def __init__(self, cfg, torch, ep, workloads):
+        self.cfg, self.torch, self.ep = cfg, torch, ep
+        log(f"[bench] generating inputs for {cfg.name}")
+        send, inp = workloads.splits_inputs(cfg)
+        self.send_np, self.inp_np = send, inp
+        self.send = torch.from_numpy(send).cuda()
+        self.inp = torch.from_numpy(inp.view(np.int16)).cuda()
+        self.sp = ep.alloc_splits_plan(cfg.W)
+        self.out = torch.empty((cfg.W * cfg.R, cfg.H), dtype=torch.int16, device="cuda")
+
+    def phases(self):
+        return [("ep_plan_splits", lambda: self.ep.ep_plan_splits(self.send, self.sp)),
+                ("ep_dispatch_splits", lambda: self.ep.ep_dispatch_splits(self.inp, self.sp, self.out))]
+
+    def n_rows(self):
+        return self.cfg.W * self.cfg.R
+
+    def bytes_per_phase(self, N):
+        c = self.cfg
+        W = c.W
+        return {"ep_plan_splits": W * W * 8 * 4 + (W + 1) * 8,
+                "ep_dispatch_splits": 2 * N * c.H * 2 + 4 * W * W * 8}
+
+    def tokens(self):
+        return self.cfg.W * self.cfg.R   # rows moved
+
+    def config_record(self):
+        c = self.cfg
+        return {"workload": c.name, "W": c.W, "R": c.R, "H": c.H, "splits": "randint[0,1024) rescaled"}
+
+    def dtype(self):
+        return "bf16"
+
+    def cpu_baseline(self, reps):
+        import oracle
+        times = []
+        for _ in range(reps):
+            t0 = time.perf_counter()
+            sp = oracle.a2a_plan(self.send_np)
+            out, _ = oracle.a2a_copy(self.inp_np, sp)
+            times.append(time.perf_counter() - t0)
+            del out
+        sec = float(np.median(times))
+        n = self.cfg.W * self.cfg.R
+        return {"value": n / sec, "unit": "rows/s", "cores": 1, "kind": "oracle",
+                "sample": f"whole workload ({n} rows), serial C oracle, median of {reps}",
+                "seconds_per_step": sec}
+
+
+# --------------------------------------------------------------------------- main
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "this build runs on one GPU only: the W expert-parallel "
+                          "ranks are emulated as buffers in one GPU's HBM; run with --gpus 1"}),
+              flush=True)
+        sys.exit(2)
+    import torch
+    import combine_ep_plan_02_amd as ep
+    import workloads
+
+    cfg = workloads.CONFIGS[args.workload]
+    bench = (SplitsBench if args.workload == 3 else MoEBench)(cfg, torch, ep, workloads)
+    phases = bench.phases()
+    stream = torch.cuda.current_stream()
+
+    def step():
+        for _, fn in phases:
+            fn()
+
+    log(f"[bench] warmup {args.warmup} steps")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    assert ep.ep_device_error() == 0
+
+    # Timed region: exactly `steps` steps, synchronised on both sides.
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / args.steps
+
+    # Per-launch durations: HIP events on the launch stream around each call.
+    log("[bench] per-phase timing")
+    ev = {name: [] for name, _ in phases}
+    for _ in range(args.steps):
+        for name, fn in phases:
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev[name].append((a, b))
+    torch.cuda.synchronize()
+    phase_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
+    assert ep.ep_device_error() == 0
+
+    N = bench.n_rows()
+    bpp = bench.bytes_per_phase(N)
+    step_bytes = sum(bpp.values())
+    dominant = max(phase_ms, key=phase_ms.get)
+    ach = bpp[dominant] / (phase_ms[dominant] * 1e-3) / 1e9
+    tokens = bench.tokens()
+    rec = {
+        "metric": METRIC,
+        "value": tokens / (ms_per_step * 1e-3),
+        "unit": "tokens/s" if args.workload != 3 else "rows/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": bench.dtype(), "data": "synthetic (seeded numpy generators, see workloads.py)",
+        "config": bench.config_record(),
+        "hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "hbm_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "algorithmic_bytes_per_step": step_bytes,
+        "rows_N": N,
+        "phase_us": {k: v * 1e3 for k, v in phase_ms.items()},
+        "phase_gbps": {k: bpp[k] / (phase_ms[k] * 1e-3) / 1e9 for k in phase_ms},
+        "roofline": {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                     "algorithmic_bytes_per_launch": bpp[dominant]},
+    }
+    if not args.no_cpu_baseline:
+        log("[bench] CPU oracle baseline")
+        rec["cpu_baseline"] = bench.cpu_baseline(args.cpu_reps)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,275 @@
+"""Python binding of libep_mi355x.so (MoE expert-parallel dispatch / combine on
+one MI355X, gfx950).
+
+Argument marshalling only: every step runs in the library's HIP kernels.
+PyTorch supplies device memory and the current stream; tensors are passed as
+raw device pointers to the C ABI declared in include/ep_mi355x.h, under the
+same names (ep_plan, ep_dispatch, ep_combine, ep_plan_splits,
+ep_dispatch_splits, ...).  There is no CPU fallback: the first call into the
+library raises ImportError when libep_mi355x.so has not been built (the
+package itself stays importable so that its build module can run).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+from . import build as _build
+
+_LIB_PATH = _build.LIB
+
+EP_OK = 0
+EP_ERR_NULLPTR = 1
+EP_ERR_INVALID = 2
+EP_ERR_UNSUPPORTED = 3
+EP_ERR_WORKSPACE = 4
+EP_ERR_HIP = 5
+
+EP_BF16 = 0
+EP_FP8_E4M3FN = 1
+
+EP_DEVERR_BAD_EXPERT = 1
+EP_DEVERR_SPLITS = 2
+EP_DEVERR_PLAN_STALL = 4
+EP_DEVERR_BAD_ROW = 8
+
+_STATUS_NAMES = {1: "EP_ERR_NULLPTR", 2: "EP_ERR_INVALID", 3: "EP_ERR_UNSUPPORTED",
+                 4: "EP_ERR_WORKSPACE", 5: "EP_ERR_HIP"}
+
+EXPORTED = ("ep_supported", "ep_workspace_size", "ep_workspace_init", "ep_plan", "ep_dispatch",
+            "ep_combine", "ep_plan_splits", "ep_dispatch_splits", "ep_last_error",
+            "ep_device_error")
+
+
+class EPError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
+        self.status = status
+
+
+class _PlanT(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in (
+        "in_splits", "src_offsets", "out_splits", "dst_offsets", "expert_counts",
+        "expert_offsets", "rank_offsets", "pos", "occ")]
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError(
+            f"{_LIB_PATH} is missing: build it with `python -m combine_ep_plan_02_amd.build` "
+            "(the HIP library has no CPU fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    sig = {
+        "ep_supported": ([i32, i32, i32, i32, i32, i32], ctypes.c_int),
+        "ep_workspace_size": ([i32, i32, i32, i32], sz),
+        "ep_workspace_init": ([P, sz, P], ctypes.c_int),
+        "ep_plan": ([i32, i32, i32, i32, P, P, ctypes.POINTER(_PlanT), P, sz, P], ctypes.c_int),
+        "ep_dispatch": ([i32, i32, i32, P, P, i32, P, P, i64, P], ctypes.c_int),
+        "ep_combine": ([i32, i32, i32, P, i64, P, P, P, P], ctypes.c_int),
+        "ep_plan_splits": ([i32, P, P, P, P, P, P], ctypes.c_int),
+        "ep_dispatch_splits": ([i32, i64, i64, P, P, P, P, P, P, P], ctypes.c_int),
+        "ep_last_error": ([], ctypes.c_char_p),
+        "ep_device_error": ([P, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
+    }
+    for name, (args, res) in sig.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    return lib
+
+
+class _LazyLib:
+    """Loads libep_mi355x.so on first use; raises ImportError if it is missing."""
+
+    _handle = None
+
+    def __getattr__(self, name):
+        if _LazyLib._handle is None:
+            _LazyLib._handle = _load()
+        return getattr(_LazyLib._handle, name)
+
+
+lib = _LazyLib()
+
+
+def _stream(stream=None):
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t: torch.Tensor | None, dtype: torch.dtype | tuple | None = None, name: str = "tensor"):
+    """Device pointer of a contiguous CUDA tensor (None -> NULL)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if dtype is not None:
+        ok = t.dtype in dtype if isinstance(dtype, tuple) else t.dtype == dtype
+        if not ok:
+            raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if t.numel() and not t.is_cuda:
+        raise ValueError(f"{name} must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
+
+
+def _check(rc: int):
+    if rc != EP_OK:
+        raise EPError(rc, lib.ep_last_error().decode())
+
+
+_BITS16 = (torch.bfloat16, torch.int16, torch.uint16)
+_BITS8 = (torch.float8_e4m3fn, torch.uint8, torch.int8)
+
+
+# --------------------------------------------------------------------- 2-D path
+
+def ep_supported(T: int, K: int, E: int, W: int, H: int, out_dtype: int = EP_BF16) -> bool:
+    return bool(lib.ep_supported(T, K, E, W, H, out_dtype))
+
+
+def ep_workspace_size(T: int, K: int, E: int, W: int) -> int:
+    return int(lib.ep_workspace_size(T, K, E, W))
+
+
+def ep_workspace_init(workspace: torch.Tensor, stream=None) -> None:
+    _check(lib.ep_workspace_init(_ptr(workspace, name="workspace"), workspace.numel() * workspace.element_size(),
+                                 _stream(stream)))
+
+
+def alloc_workspace(T: int, K: int, E: int, W: int, device="cuda", stream=None) -> torch.Tensor:
+    """Allocates (torch) and initialises (library fill kernel) a plan workspace."""
+    n = ep_workspace_size(T, K, E, W)
+    if n == 0:
+        raise EPError(EP_ERR_UNSUPPORTED, f"unsupported dimensions T={T} K={K} E={E} W={W}")
+    ws = torch.empty(n, dtype=torch.uint8, device=device)
+    ep_workspace_init(ws, stream)
+    return ws
+
+
+@dataclass
+class Plan:
+    """Device outputs of ep_plan (torch tensors allocated by the caller)."""
+    in_splits: torch.Tensor
+    src_offsets: torch.Tensor
+    out_splits: torch.Tensor
+    dst_offsets: torch.Tensor
+    expert_counts: torch.Tensor
+    expert_offsets: torch.Tensor
+    rank_offsets: torch.Tensor
+    pos: torch.Tensor
+    occ: torch.Tensor | None
+
+    def as_struct(self) -> _PlanT:
+        s = _PlanT()
+        for f, _ in _PlanT._fields_:
+            t = getattr(self, f)
+            want = torch.int32 if f in ("pos", "occ") else torch.int64
+            p = _ptr(t, want, f)
+            setattr(s, f, None if p is None else p.value)
+        return s
+
+
+def alloc_plan(T: int, K: int, E: int, W: int, device="cuda", with_occ: bool = True) -> Plan:
+    i64 = dict(dtype=torch.int64, device=device)
+    ne = E // W
+    return Plan(
+        in_splits=torch.empty((W, E), **i64), src_offsets=torch.empty((W, E), **i64),
+        out_splits=torch.empty((W, ne, W), **i64), dst_offsets=torch.empty((W, E), **i64),
+        expert_counts=torch.empty(E, **i64), expert_offsets=torch.empty(E, **i64),
+        rank_offsets=torch.empty(W + 1, **i64),
+        pos=torch.empty((T, K), dtype=torch.int32, device=device),
+        occ=torch.empty((T, K), dtype=torch.int32, device=device) if with_occ else None)
+
+
+def ep_plan(topk_ids: torch.Tensor, E: int, W: int, plan: Plan, workspace: torch.Tensor,
+            active: torch.Tensor | None = None, stream=None) -> Plan:
+    T, K = topk_ids.shape
+    st = plan.as_struct()
+    _check(lib.ep_plan(T, K, E, W, _ptr(topk_ids, torch.int32, "topk_ids"),
+                       _ptr(active, (torch.uint8, torch.bool), "active"), ctypes.byref(st),
+                       _ptr(workspace, name="workspace"),
+                       workspace.numel() * workspace.element_size(), _stream(stream)))
+    return plan
+
+
+def ep_dispatch(x: torch.Tensor, pos: torch.Tensor, expand_x: torch.Tensor,
+                expand_scales: torch.Tensor | None = None, out_dtype: int = EP_BF16,
+                stream=None) -> None:
+    T, H = x.shape
+    K = pos.shape[1]
+    if pos.shape[0] != T:
+        raise ValueError("pos must be [T][K] for x [T][H]")
+    row_dt = _BITS16 if out_dtype == EP_BF16 else _BITS8
+    if expand_x.dim() != 2 or expand_x.shape[1] != H:
+        raise ValueError("expand_x must be [cap_rows][H]")
+    _check(lib.ep_dispatch(T, K, H, _ptr(x, _BITS16, "x"), _ptr(pos, torch.int32, "pos"), out_dtype,
+                           _ptr(expand_x, row_dt, "expand_x"),
+                           _ptr(expand_scales, torch.float32, "expand_scales"),
+                           expand_x.shape[0], _stream(stream)))
+
+
+def ep_combine(y: torch.Tensor, pos: torch.Tensor, weights: torch.Tensor, out: torch.Tensor,
+               stream=None) -> None:
+    T, K = pos.shape
+    cap, H = y.shape
+    if tuple(out.shape) != (T, H) or tuple(weights.shape) != (T, K):
+        raise ValueError("out must be [T][H] and weights [T][K]")
+    _check(lib.ep_combine(T, K, H, _ptr(y, _BITS16, "y"), cap, _ptr(pos, torch.int32, "pos"),
+                          _ptr(weights, torch.float32, "weights"), _ptr(out, _BITS16, "out"),
+                          _stream(stream)))
+
+
+# --------------------------------------------------------------------- 1-D path
+
+@dataclass
+class SplitsPlan:
+    src_offsets: torch.Tensor
+    out_splits: torch.Tensor
+    dst_offsets: torch.Tensor
+    rank_offsets: torch.Tensor
+
+
+def alloc_splits_plan(W: int, device="cuda") -> SplitsPlan:
+    i64 = dict(dtype=torch.int64, device=device)
+    return SplitsPlan(torch.empty((W, W), **i64), torch.empty((W, W), **i64),
+                      torch.empty((W, W), **i64), torch.empty(W + 1, **i64))
+
+
+def ep_plan_splits(in_splits: torch.Tensor, plan: SplitsPlan, stream=None) -> SplitsPlan:
+    W = in_splits.shape[0]
+    _check(lib.ep_plan_splits(W, _ptr(in_splits, torch.int64, "in_splits"),
+                              _ptr(plan.src_offsets, torch.int64, "src_offsets"),
+                              _ptr(plan.out_splits, torch.int64, "out_splits"),
+                              _ptr(plan.dst_offsets, torch.int64, "dst_offsets"),
+                              _ptr(plan.rank_offsets, torch.int64, "rank_offsets"), _stream(stream)))
+    return plan
+
+
+def ep_dispatch_splits(inp: torch.Tensor, plan: SplitsPlan, out: torch.Tensor, stream=None) -> None:
+    """inp [W][R][...] rows, out [W*R][...] rows of the same row size."""
+    W, R = inp.shape[:2]
+    stride = inp[0, 0].numel() * inp.element_size() if R else 16
+    if out.shape[0] != W * R or (R and out[0].numel() * out.element_size() != stride):
+        raise ValueError("out must hold W*R rows of the input's row size")
+    _check(lib.ep_dispatch_splits(W, R, stride, _ptr(inp, name="in"),
+                                  _ptr(plan.src_offsets, torch.int64, "src_offsets"),
+                                  _ptr(plan.out_splits, torch.int64, "out_splits"),
+                                  _ptr(plan.dst_offsets, torch.int64, "dst_offsets"),
+                                  _ptr(plan.rank_offsets, torch.int64, "rank_offsets"),
+                                  _ptr(out, name="out"), _stream(stream)))
+
+
+def ep_device_error(stream=None) -> int:
+    code = ctypes.c_int32(0)
+    _check(lib.ep_device_error(_stream(stream), ctypes.byref(code)))
+    return int(code.value)
+
+
+def library_path() -> str:
+    return _LIB_PATH

@@ -1,0 +1,395 @@
+// ep_abi.hip -- host side of libep_mi355x.so: argument checks, workspace
+// layout, launch configuration.  The C ABI is declared in include/ep_mi355x.h.
+//
+// Checks run on the host before anything is enqueued and mirror the
+// validation contract of ROCm/aiter PR #6960 (contiguous 16-byte aligned
+// rows, row length a multiple of the vector width, no output aliasing an
+// input, early return on empty input) and the status classes of the CANN
+// "aclnnMoeDistributeDispatchV2" return codes.
+#include "ep_mi355x.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "ep_common.h"
+#include "ep_plan_kernels.h"
+#include "ep_row_kernels.h"
+
+#define EP_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return code;
+}
+
+int ok() {
+  g_last_error.clear();
+  return EP_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// [a, a+na) and [b, b+nb) share a byte.
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  if (!a || !b || na == 0 || nb == 0) return false;
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+int launch_status(const char* what) {
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+int check_dims(int32_t T, int32_t K, int32_t E, int32_t W) {
+  if (T < 0) return fail(EP_ERR_INVALID, "T must be >= 0 (got %d)", T);
+  if (K < 1 || K > EP_MAX_K) return fail(EP_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)", EP_MAX_K, K);
+  if (E < 1 || E > EP_MAX_E) return fail(EP_ERR_UNSUPPORTED, "E must be in [1, %d] (got %d)", EP_MAX_E, E);
+  if (W < 1) return fail(EP_ERR_UNSUPPORTED, "W must be >= 1 (got %d)", W);
+  if (E % W) return fail(EP_ERR_UNSUPPORTED, "E (%d) must be a multiple of W (%d)", E, W);
+  if (T % W) return fail(EP_ERR_UNSUPPORTED, "T (%d) must be a multiple of W (%d)", T, W);
+  if ((int64_t)T * K >= (int64_t)1 << 31) return fail(EP_ERR_UNSUPPORTED, "T*K must be < 2^31");
+  return EP_OK;
+}
+
+int check_rows(int32_t H, int32_t dtype) {
+  if (dtype != EP_BF16 && dtype != EP_FP8_E4M3FN) return fail(EP_ERR_INVALID, "unknown row dtype %d", dtype);
+  if (H < 1 || H > EP_MAX_H) return fail(EP_ERR_UNSUPPORTED, "H must be in [1, %d] (got %d)", EP_MAX_H, H);
+  const int vec = dtype == EP_BF16 ? 8 : 16;
+  if (H % vec) return fail(EP_ERR_UNSUPPORTED, "H (%d) must be a multiple of %d for this row dtype", H, vec);
+  return EP_OK;
+}
+
+struct PlanGeometry {
+  int Tw, tile_tokens, tiles_per_rank, ntiles;
+};
+
+PlanGeometry plan_geometry(int32_t T, int32_t K, int32_t W) {
+  PlanGeometry g{};
+  g.Tw = T / W;
+  if (g.Tw == 0) return g;
+  g.tile_tokens = ep::plan_tile_tokens(K, g.Tw);
+  g.tiles_per_rank = (g.Tw + g.tile_tokens - 1) / g.tile_tokens;
+  g.ntiles = g.tiles_per_rank * W;
+  return g;
+}
+
+size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Workspace: [ticket (256 B)] [flags: ntiles u32] [aggregates: ntiles x E i32]
+//            [inclusive: ntiles x E i32], each region 256-byte aligned.
+struct WorkspaceLayout {
+  size_t flags, aggregates, inclusive, total;
+};
+
+WorkspaceLayout workspace_layout(int ntiles, int E) {
+  WorkspaceLayout l{};
+  l.flags = 256;
+  l.aggregates = l.flags + round256((size_t)ntiles * 4);
+  l.inclusive = l.aggregates + round256((size_t)ntiles * E * 4);
+  l.total = l.inclusive + round256((size_t)ntiles * E * 4);
+  return l;
+}
+
+int id_bits_for(int E) {
+  int b = 0;
+  while ((1 << b) < E) ++b;
+  return b;
+}
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+}  // namespace
+
+EP_EXPORT int ep_supported(int32_t T, int32_t K, int32_t E, int32_t W, int32_t H, int32_t out_dtype) {
+  const std::string saved = g_last_error;
+  const bool yes = check_dims(T, K, E, W) == EP_OK && check_rows(H, out_dtype) == EP_OK;
+  g_last_error = saved;
+  return yes ? 1 : 0;
+}
+
+EP_EXPORT size_t ep_workspace_size(int32_t T, int32_t K, int32_t E, int32_t W) {
+  const std::string saved = g_last_error;
+  const bool good = check_dims(T, K, E, W) == EP_OK;
+  g_last_error = saved;
+  if (!good) return 0;
+  return workspace_layout(plan_geometry(T, K, W).ntiles, E).total;
+}
+
+EP_EXPORT int ep_workspace_init(void* workspace, size_t ws_bytes, void* stream) {
+  if (!workspace) return fail(EP_ERR_NULLPTR, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(EP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (ws_bytes % 4) return fail(EP_ERR_WORKSPACE, "workspace size must be a multiple of 4");
+  const size_t n = ws_bytes / 4;
+  if (n == 0) return ok();
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)blocks), dim3(256), 0, (hipStream_t)stream,
+                     (uint32_t*)workspace, n);
+  return launch_status("ep_workspace_init");
+}
+
+EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t* topk_ids,
+                      const uint8_t* active, const ep_plan_t* plan, void* workspace,
+                      size_t ws_bytes, void* stream) {
+  int rc = check_dims(T, K, E, W);
+  if (rc) return rc;
+  if (!plan) return fail(EP_ERR_NULLPTR, "plan is NULL");
+  if (!plan->in_splits || !plan->src_offsets || !plan->out_splits || !plan->dst_offsets ||
+      !plan->expert_counts || !plan->expert_offsets || !plan->rank_offsets)
+    return fail(EP_ERR_NULLPTR, "a required plan output is NULL");
+  const int64_t ncopies = (int64_t)T * K;
+  if (ncopies > 0 && (!topk_ids || !plan->pos)) return fail(EP_ERR_NULLPTR, "topk_ids or pos is NULL");
+  if (!workspace) return fail(EP_ERR_NULLPTR, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(EP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const PlanGeometry g = plan_geometry(T, K, W);
+  const WorkspaceLayout l = workspace_layout(g.ntiles, E);
+  if (ws_bytes < l.total)
+    return fail(EP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, l.total);
+
+  const int64_t* outs64[] = {plan->in_splits, plan->src_offsets, plan->out_splits, plan->dst_offsets,
+                             plan->expert_counts, plan->expert_offsets, plan->rank_offsets};
+  const size_t n64[] = {(size_t)W * E, (size_t)W * E, (size_t)W * E, (size_t)W * E, (size_t)E,
+                        (size_t)E, (size_t)W + 1};
+  for (int i = 0; i < 7; ++i)
+    if (!aligned(outs64[i], 8)) return fail(EP_ERR_INVALID, "plan int64 outputs must be 8-byte aligned");
+  if (!aligned(topk_ids, 4) || !aligned(plan->pos, 4) || !aligned(plan->occ, 4))
+    return fail(EP_ERR_INVALID, "topk_ids, pos and occ must be 4-byte aligned");
+  // No output may overlap an input or another output.
+  struct Range { const void* p; size_t n; const char* name; };
+  const Range ranges[] = {
+      {topk_ids, (size_t)ncopies * 4, "topk_ids"}, {active, active ? (size_t)T : 0, "active"},
+      {workspace, l.total, "workspace"}, {plan->pos, (size_t)ncopies * 4, "pos"},
+      {plan->occ, plan->occ ? (size_t)ncopies * 4 : 0, "occ"},
+      {outs64[0], n64[0] * 8, "in_splits"}, {outs64[1], n64[1] * 8, "src_offsets"},
+      {outs64[2], n64[2] * 8, "out_splits"}, {outs64[3], n64[3] * 8, "dst_offsets"},
+      {outs64[4], n64[4] * 8, "expert_counts"}, {outs64[5], n64[5] * 8, "expert_offsets"},
+      {outs64[6], n64[6] * 8, "rank_offsets"}};
+  const int nr = sizeof ranges / sizeof ranges[0];
+  for (int i = 0; i < nr; ++i)
+    for (int j = (i < 2 ? 2 : i + 1); j < nr; ++j)
+      if (overlap(ranges[i].p, ranges[i].n, ranges[j].p, ranges[j].n))
+        return fail(EP_ERR_INVALID, "%s overlaps %s", ranges[i].name, ranges[j].name);
+
+  hipStream_t s = (hipStream_t)stream;
+  uint8_t* ws = (uint8_t*)workspace;
+  uint32_t* ticket = (uint32_t*)ws;
+  uint32_t* flags = (uint32_t*)(ws + l.flags);
+  int32_t* aggregates = (int32_t*)(ws + l.aggregates);
+  int32_t* inclusive = (int32_t*)(ws + l.inclusive);
+
+  if (g.ntiles > 0) {
+    const size_t lds = (size_t)(ep::kPlanWaves + 1) * E * sizeof(int32_t);
+    hipLaunchKernelGGL(ep::plan_tile_kernel, dim3(g.ntiles), dim3(ep::kPlanThreads), lds, s, topk_ids,
+                       active, K, E, g.Tw, g.tile_tokens, g.tiles_per_rank, g.ntiles, id_bits_for(E),
+                       plan->pos, ticket, flags, aggregates, inclusive);
+    rc = launch_status("ep_plan (tile kernel)");
+    if (rc) return rc;
+  }
+  const int64_t per_block = (int64_t)ep::kFinalizeThreads * ep::kFinalizeCopiesPerThread;
+  int64_t blocks = (ncopies + per_block - 1) / per_block;
+  if (blocks < W) blocks = W;
+  hipLaunchKernelGGL(ep::plan_finalize_kernel, dim3((unsigned)blocks), dim3(ep::kFinalizeThreads), 0, s,
+                     topk_ids, ncopies, K, E, W, g.Tw > 0 ? g.Tw : 1, g.tiles_per_rank, g.ntiles,
+                     aggregates, inclusive, flags, ticket, plan->pos, plan->occ, plan->in_splits,
+                     plan->src_offsets, plan->out_splits, plan->dst_offsets, plan->expert_counts,
+                     plan->expert_offsets, plan->rank_offsets);
+  return launch_status("ep_plan (finalize kernel)");
+}
+
+EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, const int32_t* pos,
+                          int32_t out_dtype, void* expand_x, float* expand_scales, int64_t cap_rows,
+                          void* stream) {
+  if (T < 0) return fail(EP_ERR_INVALID, "T must be >= 0 (got %d)", T);
+  if (K < 1 || K > EP_MAX_K) return fail(EP_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)", EP_MAX_K, K);
+  int rc = check_rows(H, out_dtype);
+  if (rc) return rc;
+  if ((int64_t)T * K >= (int64_t)1 << 31) return fail(EP_ERR_UNSUPPORTED, "T*K must be < 2^31");
+  if (cap_rows < (int64_t)T * K)
+    return fail(EP_ERR_INVALID, "cap_rows (%lld) must be >= T*K (%lld)", (long long)cap_rows,
+                (long long)T * K);
+  if (T == 0) return ok();
+  if (!x || !pos || !expand_x) return fail(EP_ERR_NULLPTR, "x, pos and expand_x are required");
+  const bool fp8 = out_dtype == EP_FP8_E4M3FN;
+  if (fp8 && !expand_scales) return fail(EP_ERR_NULLPTR, "expand_scales is required for fp8 rows");
+  if (!aligned(x, 16) || !aligned(expand_x, 16))
+    return fail(EP_ERR_INVALID, "x and expand_x must be 16-byte aligned");
+  if (!aligned(pos, 4) || (fp8 && !aligned(expand_scales, 4)))
+    return fail(EP_ERR_INVALID, "pos and expand_scales must be 4-byte aligned");
+  const size_t xb = (size_t)T * H * 2, pb = (size_t)T * K * 4;
+  const size_t eb = (size_t)cap_rows * H * (fp8 ? 1 : 2);
+  const size_t sb = fp8 ? (size_t)cap_rows * 4 : 0;
+  if (overlap(expand_x, eb, x, xb) || overlap(expand_x, eb, pos, pb))
+    return fail(EP_ERR_INVALID, "expand_x overlaps an input");
+  if (fp8 && (overlap(expand_scales, sb, x, xb) || overlap(expand_scales, sb, pos, pb) ||
+              overlap(expand_scales, sb, expand_x, eb)))
+    return fail(EP_ERR_INVALID, "expand_scales overlaps another buffer");
+
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)((T + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock));
+  const dim3 block(ep::kRowThreads);
+  if (!fp8) {
+    const int V = H / 8;
+    const ep::u32x4* xv = (const ep::u32x4*)x;
+    ep::u32x4* ev = (ep::u32x4*)expand_x;
+    const int per_lane = (V + ep::kWave - 1) / ep::kWave;
+    if (per_lane <= 1)
+      hipLaunchKernelGGL(ep::dispatch_bf16_kernel<1>, grid, block, 0, s, xv, pos, ev, T, K, V, cap_rows);
+    else if (per_lane <= 2)
+      hipLaunchKernelGGL(ep::dispatch_bf16_kernel<2>, grid, block, 0, s, xv, pos, ev, T, K, V, cap_rows);
+    else if (per_lane <= 4)
+      hipLaunchKernelGGL(ep::dispatch_bf16_kernel<4>, grid, block, 0, s, xv, pos, ev, T, K, V, cap_rows);
+    else if (per_lane <= 8)
+      hipLaunchKernelGGL(ep::dispatch_bf16_kernel<8>, grid, block, 0, s, xv, pos, ev, T, K, V, cap_rows);
+    else
+      hipLaunchKernelGGL(ep::dispatch_bf16_kernel<16>, grid, block, 0, s, xv, pos, ev, T, K, V, cap_rows);
+    return launch_status("ep_dispatch (bf16)");
+  }
+  const int NG = H / 16;
+  const ep::u32x4* xv = (const ep::u32x4*)x;
+  ep::u32x4* qv = (ep::u32x4*)expand_x;
+  const int per_lane = (NG + ep::kWave - 1) / ep::kWave;
+  if (per_lane <= 1)
+    hipLaunchKernelGGL(ep::dispatch_fp8_kernel<1>, grid, block, 0, s, xv, pos, qv, expand_scales, T, K, NG, cap_rows);
+  else if (per_lane <= 2)
+    hipLaunchKernelGGL(ep::dispatch_fp8_kernel<2>, grid, block, 0, s, xv, pos, qv, expand_scales, T, K, NG, cap_rows);
+  else if (per_lane <= 4)
+    hipLaunchKernelGGL(ep::dispatch_fp8_kernel<4>, grid, block, 0, s, xv, pos, qv, expand_scales, T, K, NG, cap_rows);
+  else
+    hipLaunchKernelGGL(ep::dispatch_fp8_kernel<8>, grid, block, 0, s, xv, pos, qv, expand_scales, T, K, NG, cap_rows);
+  return launch_status("ep_dispatch (fp8)");
+}
+
+EP_EXPORT int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t* y, int64_t cap_rows,
+                         const int32_t* pos, const float* weights, uint16_t* out, void* stream) {
+  if (T < 0) return fail(EP_ERR_INVALID, "T must be >= 0 (got %d)", T);
+  if (K < 1 || K > EP_MAX_K) return fail(EP_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)", EP_MAX_K, K);
+  int rc = check_rows(H, EP_BF16);
+  if (rc) return rc;
+  if ((int64_t)T * K >= (int64_t)1 << 31) return fail(EP_ERR_UNSUPPORTED, "T*K must be < 2^31");
+  if (cap_rows < 0) return fail(EP_ERR_INVALID, "cap_rows must be >= 0");
+  if (T == 0) return ok();
+  if (!y || !pos || !weights || !out) return fail(EP_ERR_NULLPTR, "y, pos, weights and out are required");
+  if (!aligned(y, 16) || !aligned(out, 16)) return fail(EP_ERR_INVALID, "y and out must be 16-byte aligned");
+  if (!aligned(pos, 4) || !aligned(weights, 4)) return fail(EP_ERR_INVALID, "pos and weights must be 4-byte aligned");
+  const size_t ob = (size_t)T * H * 2;
+  if (overlap(out, ob, y, (size_t)cap_rows * H * 2) || overlap(out, ob, pos, (size_t)T * K * 4) ||
+      overlap(out, ob, weights, (size_t)T * K * 4))
+    return fail(EP_ERR_INVALID, "out overlaps an input");
+
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)((T + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock));
+  const dim3 block(ep::kRowThreads);
+  const int V = H / 8;
+  const ep::u32x4* yv = (const ep::u32x4*)y;
+  ep::u32x4* ov = (ep::u32x4*)out;
+  if (K <= 4)
+    hipLaunchKernelGGL((ep::combine_kernel<4, 4>), grid, block, 0, s, yv, pos, weights, ov, T, K, V, cap_rows);
+  else if (K <= 8)
+    hipLaunchKernelGGL((ep::combine_kernel<8, 2>), grid, block, 0, s, yv, pos, weights, ov, T, K, V, cap_rows);
+  else
+    hipLaunchKernelGGL((ep::combine_kernel<16, 1>), grid, block, 0, s, yv, pos, weights, ov, T, K, V, cap_rows);
+  return launch_status("ep_combine");
+}
+
+EP_EXPORT int ep_plan_splits(int32_t W, const int64_t* in_splits, int64_t* src_offsets,
+                             int64_t* out_splits, int64_t* dst_offsets, int64_t* rank_offsets,
+                             void* stream) {
+  if (W < 1 || W > EP_MAX_SPLITS_W)
+    return fail(EP_ERR_UNSUPPORTED, "W must be in [1, %d] (got %d)", EP_MAX_SPLITS_W, W);
+  if (!in_splits || !src_offsets || !out_splits || !dst_offsets || !rank_offsets)
+    return fail(EP_ERR_NULLPTR, "all plan arrays are required");
+  const void* ps[] = {in_splits, src_offsets, out_splits, dst_offsets, rank_offsets};
+  const size_t ns[] = {(size_t)W * W * 8, (size_t)W * W * 8, (size_t)W * W * 8, (size_t)W * W * 8,
+                       (size_t)(W + 1) * 8};
+  for (int i = 0; i < 5; ++i) {
+    if (!aligned(ps[i], 8)) return fail(EP_ERR_INVALID, "split arrays must be 8-byte aligned");
+    for (int j = i + 1; j < 5; ++j)
+      if (overlap(ps[i], ns[i], ps[j], ns[j])) return fail(EP_ERR_INVALID, "split arrays overlap");
+  }
+  hipLaunchKernelGGL(ep::plan_splits_kernel, dim3(1), dim3(ep::kSplitsPlanThreads), 0, (hipStream_t)stream,
+                     W, in_splits, src_offsets, out_splits, dst_offsets, rank_offsets);
+  return launch_status("ep_plan_splits");
+}
+
+EP_EXPORT int ep_dispatch_splits(int32_t W, int64_t R, int64_t stride_bytes, const void* in,
+                                 const int64_t* src_offsets, const int64_t* out_splits,
+                                 const int64_t* dst_offsets, const int64_t* rank_offsets, void* out,
+                                 void* stream) {
+  if (W < 1 || W > EP_MAX_SPLITS_W)
+    return fail(EP_ERR_UNSUPPORTED, "W must be in [1, %d] (got %d)", EP_MAX_SPLITS_W, W);
+  if (R < 0) return fail(EP_ERR_INVALID, "R must be >= 0");
+  if (stride_bytes <= 0 || stride_bytes % 16)
+    return fail(EP_ERR_UNSUPPORTED, "stride_bytes must be a positive multiple of 16 (got %lld)",
+                (long long)stride_bytes);
+  if (R == 0) return ok();
+  if (!in || !out || !src_offsets || !out_splits || !dst_offsets || !rank_offsets)
+    return fail(EP_ERR_NULLPTR, "all buffers are required");
+  if (!aligned(in, 16) || !aligned(out, 16)) return fail(EP_ERR_INVALID, "in and out must be 16-byte aligned");
+  const size_t bytes = (size_t)W * R * stride_bytes;
+  if (overlap(in, bytes, out, bytes)) return fail(EP_ERR_INVALID, "out overlaps in");
+  const int64_t* plan[] = {src_offsets, out_splits, dst_offsets, rank_offsets};
+  const size_t plan_bytes[] = {(size_t)W * W * 8, (size_t)W * W * 8, (size_t)W * W * 8,
+                               (size_t)(W + 1) * 8};
+  for (int i = 0; i < 4; ++i)
+    if (overlap(out, bytes, plan[i], plan_bytes[i]))
+      return fail(EP_ERR_INVALID, "out overlaps a plan array");
+  const int64_t Vr = stride_bytes / 16;
+  const int chunks = W * W;
+  int bpc = (2048 + chunks - 1) / chunks;
+  const int64_t max_rows_per_chunk = R;  // no chunk holds more than its sender's R rows
+  const int64_t need = (max_rows_per_chunk + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock;
+  if (bpc > need) bpc = (int)need;
+  if (bpc < 1) bpc = 1;
+  const dim3 grid(chunks, bpc);
+  hipStream_t s = (hipStream_t)stream;
+  const ep::u32x4* iv = (const ep::u32x4*)in;
+  ep::u32x4* ov = (ep::u32x4*)out;
+  const int64_t per_lane = (Vr + ep::kWave - 1) / ep::kWave;
+  if (per_lane <= 1)
+    hipLaunchKernelGGL(ep::copy_splits_kernel<1>, grid, dim3(ep::kRowThreads), 0, s, iv, ov, src_offsets,
+                       out_splits, dst_offsets, rank_offsets, W, R, Vr);
+  else if (per_lane <= 2)
+    hipLaunchKernelGGL(ep::copy_splits_kernel<2>, grid, dim3(ep::kRowThreads), 0, s, iv, ov, src_offsets,
+                       out_splits, dst_offsets, rank_offsets, W, R, Vr);
+  else if (per_lane <= 4)
+    hipLaunchKernelGGL(ep::copy_splits_kernel<4>, grid, dim3(ep::kRowThreads), 0, s, iv, ov, src_offsets,
+                       out_splits, dst_offsets, rank_offsets, W, R, Vr);
+  else
+    hipLaunchKernelGGL(ep::copy_splits_kernel<8>, grid, dim3(ep::kRowThreads), 0, s, iv, ov, src_offsets,
+                       out_splits, dst_offsets, rank_offsets, W, R, Vr);
+  return launch_status("ep_dispatch_splits");
+}
+
+EP_EXPORT const char* ep_last_error(void) { return g_last_error.c_str(); }
+
+EP_EXPORT int ep_device_error(void* stream, int32_t* code) {
+  if (!code) return fail(EP_ERR_NULLPTR, "code is NULL");
+  hipError_t e = hipStreamSynchronize((hipStream_t)stream);
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "stream synchronize failed: %s", hipGetErrorString(e));
+  unsigned int v = 0;
+  e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(ep::g_device_error), sizeof v, 0, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "reading the device error word failed: %s", hipGetErrorString(e));
+  const unsigned int zero = 0;
+  e = hipMemcpyToSymbol(HIP_SYMBOL(ep::g_device_error), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "clearing the device error word failed: %s", hipGetErrorString(e));
+  *code = (int32_t)v;
+  return ok();
+}

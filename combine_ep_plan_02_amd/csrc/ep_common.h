@@ -1,0 +1,54 @@
+// ep_common.h -- shared device helpers of the gfx950 dispatch / combine kernels.
+//
+// Wave64 throughout: every kernel is written for 64-lane wavefronts (CDNA4),
+// rows move as 16-byte vectors (global_load/store_dwordx4).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ep {
+
+constexpr int kWave = 64;
+
+// 16-byte vector as a clang ext-vector so the non-temporal builtins accept it.
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Device error word: one per device, sticky until ep_device_error() reads it.
+__device__ unsigned int g_device_error;
+
+constexpr unsigned kErrBadExpert = 1u;   // EP_DEVERR_BAD_EXPERT
+constexpr unsigned kErrSplits = 2u;      // EP_DEVERR_SPLITS
+constexpr unsigned kErrPlanStall = 4u;   // the plan's look-back gave up waiting
+constexpr unsigned kErrBadRow = 8u;      // a position outside the row capacity
+
+__device__ __forceinline__ void raise_device_error(unsigned bits) {
+  __hip_atomic_fetch_or(&g_device_error, bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// Wave-uniform copy of a value held identically by all active lanes.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+// Lanes strictly below this one.
+__device__ __forceinline__ uint64_t lanemask_lt() {
+  const int l = lane_id();
+  return l == 0 ? 0ull : (~0ull >> (64 - l));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
+
+// bf16 <-> fp32.  bf16 is the upper half of a binary32; the narrowing rounds
+// to nearest, ties to even, keeping NaNs quiet.
+__device__ __forceinline__ float bf16lo(uint32_t packed) { return __uint_as_float(packed << 16); }
+__device__ __forceinline__ float bf16hi(uint32_t packed) { return __uint_as_float(packed & 0xffff0000u); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+}  // namespace ep

@@ -1,0 +1,325 @@
+// ep_plan_kernels.h -- exchange plan, stable occurrences and positions.
+//
+// What is computed (PyTorch compare view "ciflow/h100-symm-mem/166772":
+// make2dExchangePlan, get_occurrence_numbers, _allToAllV_2d_index_push_kernel):
+// split counts per (source rank, expert), their scans, the transposed
+// out_splits, and for every live copy (t,k) its global expandX row
+//   pos = expert_offsets[e] + #(earlier live copies of expert e, all ranks)
+// which equals rank_offsets[d] + dst_offsets[s][e] + occurrence.
+//
+// Two kernels:
+//  1. plan_tile_kernel -- one workgroup per tile of tokens of one source rank.
+//     Each wave ranks its 64-copy chunks in order with a ballot-based
+//     match-any over the expert-id bits (stable, no LDS atomics), keeping a
+//     private per-wave histogram in LDS; waves are combined in wave order.
+//     The tile's histogram is then scanned across tiles with a decoupled
+//     look-back (tile ids from an atomic ticket, so every predecessor is
+//     already running): each tile publishes its aggregate, accumulates
+//     predecessors' aggregates until it meets an inclusive prefix, then
+//     publishes its own inclusive prefix.  It writes, per copy, the number
+//     of earlier live copies of the same expert over all tiles (a partial
+//     position, into pos).
+//  2. plan_finalize_kernel -- every workgroup rescans the E expert totals
+//     (the last tile's inclusive prefix) to get expert_offsets; workgroup s<W
+//     writes rank s's rows of the W x E plan arrays; all workgroups turn the
+//     partial positions into final positions and occurrences.  Workgroup 0
+//     returns the look-back flags and ticket to zero for the next call.
+#pragma once
+
+#include "ep_common.h"
+
+namespace ep {
+
+constexpr int kPlanThreads = 512;
+constexpr int kPlanWaves = kPlanThreads / kWave;           // 8
+constexpr int kPlanChunks = 4;                              // 64-copy chunks per wave
+constexpr int kPlanTileCopies = kPlanWaves * kWave * kPlanChunks;  // 2048
+
+constexpr uint32_t kFlagAggregate = 1u;
+constexpr uint32_t kFlagInclusive = 2u;
+constexpr int kSpinLimit = 1 << 20;  // bounded polling: the kernel always exits
+
+constexpr int kFinalizeThreads = 256;
+constexpr int kFinalizeCopiesPerThread = 4;
+
+// Tokens per tile: as many as fit kPlanTileCopies copies, never crossing a
+// source rank boundary.
+inline int plan_tile_tokens(int K, int Tw) {
+  int tt = kPlanTileCopies / K;
+  if (tt < 1) tt = 1;
+  if (tt > Tw) tt = Tw;
+  return tt < 1 ? 1 : tt;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_tile_kernel(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ active, int K, int E,
+    int Tw, int tile_tokens, int tiles_per_rank, int ntiles, int id_bits,
+    int32_t* __restrict__ pos_partial, uint32_t* ticket, uint32_t* flags,
+    int32_t* aggregates, int32_t* inclusive) {
+  extern __shared__ int32_t lds[];
+  int32_t* hist = lds;                      // [kPlanWaves][E]: counts, then wave-exclusive
+  int32_t* tile_excl = lds + kPlanWaves * E;  // [E]: copies of e in earlier tiles
+  __shared__ int s_tile;
+  __shared__ uint32_t s_status;
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+
+  if (tid == 0) s_tile = (int)__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) hist[i] = 0;
+  __syncthreads();
+  const int b = s_tile;
+  if (b >= ntiles) {  // only possible with a workspace that was never initialised
+    if (tid == 0) raise_device_error(kErrPlanStall);
+    return;
+  }
+
+  const int s = b / tiles_per_rank;
+  const int j = b - s * tiles_per_rank;
+  const int64_t t0 = (int64_t)s * Tw + (int64_t)j * tile_tokens;
+  int64_t t1 = t0 + tile_tokens;
+  if (t1 > (int64_t)(s + 1) * Tw) t1 = (int64_t)(s + 1) * Tw;
+  const int64_t c0 = t0 * K;
+  const int n = (int)((t1 - t0) * K);
+  const int seg = (n + kPlanWaves - 1) / kPlanWaves;
+  const int cs = wave * seg;                       // wave's first copy, tile-relative
+  const int ce = min(cs + seg, n);
+
+  // Stable in-wave ranking, chunk by chunk, in flattened (t,k) order.
+  int32_t* myhist = hist + wave * E;
+  int e_reg[kPlanChunks];
+  int r_reg[kPlanChunks];
+#pragma unroll
+  for (int ch = 0; ch < kPlanChunks; ++ch) {
+    const int c = cs + ch * kWave + lane;
+    const bool valid = c < ce;
+    int e = -1;
+    bool live = false;
+    if (valid) {
+      const int64_t gc = c0 + c;
+      e = ids[gc];
+      const bool act = active == nullptr || active[gc / K] != 0;
+      if (act) {
+        live = (unsigned)e < (unsigned)E;
+        if (!live) raise_device_error(kErrBadExpert);
+      }
+    }
+    uint64_t peers = ballot(live);
+    for (int bit = 0; bit < id_bits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t ones = ballot(live && set);
+      peers &= set ? ones : ~ones;
+    }
+    int r = 0;
+    if (live) {
+      const int below = __popcll(peers & lanemask_lt());
+      const int base = myhist[e];
+      r = base + below;
+      if ((peers >> lane) == 1ull) myhist[e] = base + __popcll(peers);  // highest peer
+    }
+    e_reg[ch] = live ? e : -1;
+    r_reg[ch] = r;
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+
+  // Combine waves in wave order: hist[w][e] becomes the wave-exclusive prefix.
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const int v = hist[w * E + e];
+      hist[w * E + e] = run;
+      run += v;
+    }
+    tile_excl[e] = run;  // the tile's aggregate for now
+  }
+  __syncthreads();
+
+  // Decoupled look-back across tiles.
+  if (b == 0) {
+    for (int e = tid; e < E; e += kPlanThreads) {
+      inclusive[e] = tile_excl[e];
+      tile_excl[e] = 0;
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(&flags[0], kFlagInclusive, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  } else {
+    for (int e = tid; e < E; e += kPlanThreads) aggregates[(int64_t)b * E + e] = tile_excl[e];
+    __threadfence();
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(&flags[b], kFlagAggregate, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+
+    // Each thread owns experts tid, tid + 512 (E <= 1024).
+    int ex0 = 0, ex1 = 0;
+    int p = b - 1;
+    while (true) {
+      if (tid == 0) {
+        uint32_t st = 0;
+        for (int spin = 0; spin < kSpinLimit; ++spin) {
+          st = __hip_atomic_load(&flags[p], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+          if (st != 0) break;
+          __builtin_amdgcn_s_sleep(1);
+        }
+        if (st == 0) raise_device_error(kErrPlanStall);
+        s_status = st;
+      }
+      __syncthreads();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+      const uint32_t st = s_status;
+      const int32_t* src = (st == kFlagInclusive) ? inclusive : aggregates;
+      if (st != 0) {
+        if (tid < E) ex0 += src[(int64_t)p * E + tid];
+        if (tid + kPlanThreads < E) ex1 += src[(int64_t)p * E + tid + kPlanThreads];
+      }
+      __syncthreads();  // s_status is rewritten by the next poll
+      if (st == kFlagInclusive || st == 0 || p == 0) break;
+      --p;
+    }
+    if (tid < E) {
+      inclusive[(int64_t)b * E + tid] = ex0 + tile_excl[tid];
+      tile_excl[tid] = ex0;
+    }
+    if (tid + kPlanThreads < E) {
+      inclusive[(int64_t)b * E + tid + kPlanThreads] = ex1 + tile_excl[tid + kPlanThreads];
+      tile_excl[tid + kPlanThreads] = ex1;
+    }
+    __threadfence();
+    __syncthreads();
+    if (tid == 0)
+      __hip_atomic_store(&flags[b], kFlagInclusive, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+
+  // Partial position: earlier live copies of the same expert over all tiles.
+#pragma unroll
+  for (int ch = 0; ch < kPlanChunks; ++ch) {
+    const int c = cs + ch * kWave + lane;
+    if (c < ce) {
+      const int e = e_reg[ch];
+      pos_partial[c0 + c] = e >= 0 ? tile_excl[e] + myhist[e] + r_reg[ch] : -1;
+    }
+  }
+}
+
+// Block-wide exclusive scan of n <= 1024 ints held in LDS `a` (in place);
+// returns the total.  256 threads, 4 consecutive values per thread.
+__device__ int block_exclusive_scan_1024(int32_t* a, int n, int32_t* wave_sums) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  int v[4];
+  int local = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid * 4 + i;
+    v[i] = idx < n ? a[idx] : 0;
+    local += v[i];
+  }
+  // inclusive scan of `local` across the wave
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) wave_sums[wave] = incl;
+  __syncthreads();
+  int wave_base = 0;
+  int total = 0;
+#pragma unroll
+  for (int w = 0; w < kFinalizeThreads / kWave; ++w) {
+    const int ws = wave_sums[w];
+    if (w < wave) wave_base += ws;
+    total += ws;
+  }
+  int run = wave_base + incl - local;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int idx = tid * 4 + i;
+    if (idx < n) a[idx] = run;
+    run += v[i];
+  }
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kFinalizeThreads) void plan_finalize_kernel(
+    const int32_t* __restrict__ ids, int64_t n_copies, int K, int E, int W, int Tw,
+    int tiles_per_rank, int ntiles, const int32_t* __restrict__ aggregates,
+    const int32_t* __restrict__ inclusive, uint32_t* flags, uint32_t* ticket,
+    int32_t* __restrict__ pos, int32_t* __restrict__ occ, int64_t* __restrict__ in_splits,
+    int64_t* __restrict__ src_offsets, int64_t* __restrict__ out_splits,
+    int64_t* __restrict__ dst_offsets, int64_t* __restrict__ expert_counts,
+    int64_t* __restrict__ expert_offsets, int64_t* __restrict__ rank_offsets) {
+  __shared__ int32_t eoff[1024];
+  __shared__ int32_t row[1024];
+  __shared__ int32_t wave_sums[kFinalizeThreads / kWave];
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x;
+  const int ne = E / W;
+  const int32_t* totals = ntiles > 0 ? inclusive + (int64_t)(ntiles - 1) * E : nullptr;
+
+  for (int e = tid; e < E; e += kFinalizeThreads) eoff[e] = totals ? totals[e] : 0;
+  __syncthreads();
+  const int n_live = block_exclusive_scan_1024(eoff, E, wave_sums);
+
+  if (g == 0) {
+    for (int e = tid; e < E; e += kFinalizeThreads) {
+      expert_counts[e] = totals ? totals[e] : 0;
+      expert_offsets[e] = eoff[e];
+    }
+    for (int d = tid; d <= W; d += kFinalizeThreads)
+      rank_offsets[d] = d < W ? eoff[d * ne] : n_live;
+  }
+
+  if (g < W) {  // rank s = g's rows of the W x E arrays
+    const int s = g;
+    const int first = s * tiles_per_rank;
+    const int last = first + tiles_per_rank - 1;
+    for (int e = tid; e < E; e += kFinalizeThreads) {
+      int base = 0, cnt = 0;
+      if (ntiles > 0) {
+        base = inclusive[(int64_t)first * E + e] - (first > 0 ? aggregates[(int64_t)first * E + e]
+                                                              : inclusive[e]);
+        cnt = inclusive[(int64_t)last * E + e] - base;
+      }
+      row[e] = cnt;
+      in_splits[(int64_t)s * E + e] = cnt;
+      out_splits[(int64_t)e * W + s] = cnt;
+      dst_offsets[(int64_t)s * E + e] = base + eoff[e] - eoff[(e / ne) * ne];
+    }
+    __syncthreads();
+    block_exclusive_scan_1024(row, E, wave_sums);
+    for (int e = tid; e < E; e += kFinalizeThreads) src_offsets[(int64_t)s * E + e] = row[e];
+  }
+
+  // Final positions and occurrences.
+  const int64_t per_block = (int64_t)kFinalizeThreads * kFinalizeCopiesPerThread;
+  const int64_t cbeg = (int64_t)g * per_block;
+  for (int64_t c = cbeg + tid; c < n_copies && c < cbeg + per_block; c += kFinalizeThreads) {
+    const int p = pos[c];
+    if (p >= 0) {
+      const int e = ids[c];
+      const int s = (int)((c / K) / Tw);
+      const int first = s * tiles_per_rank;
+      // copies of e before rank s = exclusive prefix of rank s's first tile
+      const int before_rank = first > 0 ? inclusive[(int64_t)first * E + e] - aggregates[(int64_t)first * E + e] : 0;
+      pos[c] = eoff[e] + p;
+      if (occ) occ[c] = p - before_rank;
+    } else if (occ) {
+      occ[c] = -1;
+    }
+  }
+
+  if (g == 0) {
+    for (int i = tid; i < ntiles; i += kFinalizeThreads) flags[i] = 0;
+    if (tid == 0) *ticket = 0;
+  }
+}
+
+}  // namespace ep

@@ -1,0 +1,334 @@
+// ep_row_kernels.h -- HBM-bound row movers: dispatch scatter (bf16 and
+// per-token dynamic fp8), weighted combine gather, and the 1-D uneven
+// all-to-all (plan + chunk copy).
+//
+// Token-major, one wavefront per token: a token's positions (K <= 16) are read
+// once by the first K lanes and broadcast with v_readlane, so the row loop
+// carries no per-element index math; every row moves as 16-byte vectors, 64
+// lanes side by side (1 KiB per wave instruction), fully coalesced.
+#pragma once
+
+#include "ep_common.h"
+
+namespace ep {
+
+constexpr int kRowThreads = 256;                       // 4 waves
+constexpr int kTokensPerBlock = kRowThreads / kWave;   // one token per wave
+
+// Lane k < K of a token's wave reads pos[t][k]; a row outside [0, cap_rows)
+// other than -1 is a caller error: it is dropped and flagged, never followed.
+__device__ __forceinline__ int row_of(const int32_t* __restrict__ pos, int t, int K, int lane,
+                                      int64_t cap_rows) {
+  if (lane >= K) return -1;
+  const int p = pos[(int64_t)t * K + lane];
+  if (p >= 0 && (int64_t)p >= cap_rows) {
+    raise_device_error(kErrBadRow);
+    return -1;
+  }
+  return p < 0 ? -1 : p;
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch, bf16 rows: expand_x[pos[t][k]] = x[t] for every live copy
+// (_allToAllV_2d_index_push_kernel on the PyTorch compare view
+// "ciflow/h100-symm-mem/166772" puts one row per (token, k)).  x is read once
+// per token, each row is written K times.
+// ---------------------------------------------------------------------------
+template <int U>
+__global__ __launch_bounds__(kRowThreads) void dispatch_bf16_kernel(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ ex,
+    int T, int K, int V, int64_t cap_rows) {
+  const int t = uniform(blockIdx.x * kTokensPerBlock + (int)(threadIdx.x / kWave));
+  if (t >= T) return;
+  const int lane = lane_id();
+  const int my_pos = row_of(pos, t, K, lane, cap_rows);
+  const uint64_t live = ballot(my_pos >= 0);
+  if (live == 0) return;  // inactive token: x is not read
+  const u32x4* src = x + (int64_t)t * V;
+  for (int v0 = 0; v0 < V; v0 += kWave * U) {
+    u32x4 r[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = v0 + u * kWave + lane;
+      if (idx < V) r[u] = src[idx];
+    }
+    uint64_t m = live;
+    while (m) {
+      const int k = __builtin_ctzll(m);
+      m &= m - 1;
+      const int p = __builtin_amdgcn_readlane(my_pos, k);
+      u32x4* dst = ex + (int64_t)p * V;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = v0 + u * kWave + lane;
+        if (idx < V) __builtin_nontemporal_store(r[u], dst + idx);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch with per-token dynamic quantisation to OCP fp8 E4M3FN (quantMode 2
+// of the CANN "aclnnMoeDistributeDispatchV2" page; one fp32 scale per
+// expanded row, as dynamicScalesOut):
+//   scale = fl32(amax / 448),  code = E4M3FN_rne_sat(fl32(x / scale)).
+// The row is read once; the first G groups of 16 values per lane stay in
+// VGPRs between the amax pass and the quantise pass (G*64*16 >= H covers
+// rows up to G*1024 values), longer rows re-read the rest.
+// ---------------------------------------------------------------------------
+
+// fp32 -> E4M3FN, round to nearest even, saturating to +-448; NaN -> 0x7f.
+__device__ __forceinline__ uint32_t e4m3fn_code(float v) {
+  const uint32_t u = __float_as_uint(v);
+  const uint32_t sign = (u >> 24) & 0x80u;
+  const uint32_t a = u & 0x7fffffffu;
+  uint32_t mag;
+  if (a > 0x7f800000u) {
+    mag = 0x7fu;
+  } else if (a >= 0x43e00000u) {  // |v| >= 448 (infinity included): saturate
+    mag = 0x7eu;
+  } else if (a >= 0x3c800000u) {  // 2^-6 <= |v| < 448: normal codes
+    const uint32_t q = (((a >> 23) - 120u) << 3) | ((a >> 20) & 7u);
+    const uint32_t rest = a & 0xfffffu;
+    mag = q + ((rest > 0x80000u) | ((rest == 0x80000u) & (q & 1u)));
+  } else {  // subnormal codes are the multiples of 2^-9 below 2^-6
+    mag = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+  }
+  return sign | mag;
+}
+
+// Quantise 16 bf16 values (two 16-byte vectors) into 16 codes.
+__device__ __forceinline__ u32x4 quantize16(const u32x4 a, const u32x4 b, float scale) {
+  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = w[2 * i], hi = w[2 * i + 1];
+    const float f0 = bf16lo(lo), f1 = bf16hi(lo), f2 = bf16lo(hi), f3 = bf16hi(hi);
+    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+    if (scale != 0.0f) {
+      c0 = e4m3fn_code(f0 / scale);
+      c1 = e4m3fn_code(f1 / scale);
+      c2 = e4m3fn_code(f2 / scale);
+      c3 = e4m3fn_code(f3 / scale);
+    }
+    out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+  }
+  return u32x4{out[0], out[1], out[2], out[3]};
+}
+
+// Largest bf16 magnitude of two vectors, as the 15-bit magnitude pattern
+// (non-negative floats order like their bit patterns).
+__device__ __forceinline__ uint32_t amax16_bits(const u32x4 a, const u32x4 b, uint32_t m) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    m = max(m, w[i] & 0x7fffu);
+    m = max(m, (w[i] >> 16) & 0x7fffu);
+  }
+  return m;
+}
+
+template <int G>
+__global__ __launch_bounds__(kRowThreads) void dispatch_fp8_kernel(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ q,
+    float* __restrict__ scales, int T, int K, int NG, int64_t cap_rows) {
+  const int t = uniform(blockIdx.x * kTokensPerBlock + (int)(threadIdx.x / kWave));
+  if (t >= T) return;
+  const int lane = lane_id();
+  const int my_pos = row_of(pos, t, K, lane, cap_rows);
+  const uint64_t live = ballot(my_pos >= 0);
+  if (live == 0) return;
+  const u32x4* src = x + (int64_t)t * NG * 2;
+
+  u32x4 cache[G][2];
+  uint32_t mbits = 0;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int idx = g * kWave + lane;
+    if (idx < NG) {
+      cache[g][0] = src[2 * idx];
+      cache[g][1] = src[2 * idx + 1];
+      mbits = amax16_bits(cache[g][0], cache[g][1], mbits);
+    }
+  }
+  for (int idx = G * kWave + lane; idx < NG; idx += kWave)
+    mbits = amax16_bits(src[2 * idx], src[2 * idx + 1], mbits);
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, off, kWave));
+  const float amax = __uint_as_float(uniform((int)mbits) << 16);
+  const float scale = amax / 448.0f;
+
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int idx = g * kWave + lane;
+    if (idx < NG) {
+      const u32x4 code = quantize16(cache[g][0], cache[g][1], scale);
+      uint64_t m = live;
+      while (m) {
+        const int k = __builtin_ctzll(m);
+        m &= m - 1;
+        const int p = __builtin_amdgcn_readlane(my_pos, k);
+        __builtin_nontemporal_store(code, q + (int64_t)p * NG + idx);
+      }
+    }
+  }
+  for (int idx = G * kWave + lane; idx < NG; idx += kWave) {
+    const u32x4 code = quantize16(src[2 * idx], src[2 * idx + 1], scale);
+    uint64_t m = live;
+    while (m) {
+      const int k = __builtin_ctzll(m);
+      m &= m - 1;
+      const int p = __builtin_amdgcn_readlane(my_pos, k);
+      __builtin_nontemporal_store(code, q + (int64_t)p * NG + idx);
+    }
+  }
+  if (my_pos >= 0) scales[my_pos] = scale;
+}
+
+// ---------------------------------------------------------------------------
+// Weighted combine: out[t] = bf16_rne(sum_k w[t][k] * y[pos[t][k]]), fp32
+// fused multiply-adds in increasing k from +0; copies with pos < 0 add
+// nothing.  All K rows of a column block are loaded before the first FMA so
+// the K gathers are in flight together.
+// ---------------------------------------------------------------------------
+template <int KMAX, int U>
+__global__ __launch_bounds__(kRowThreads) void combine_kernel(
+    const u32x4* __restrict__ y, const int32_t* __restrict__ pos,
+    const float* __restrict__ w, u32x4* __restrict__ out, int T, int K, int V, int64_t cap_rows) {
+  const int t = uniform(blockIdx.x * kTokensPerBlock + (int)(threadIdx.x / kWave));
+  if (t >= T) return;
+  const int lane = lane_id();
+  const int my_pos = row_of(pos, t, K, lane, cap_rows);
+  const float my_w = lane < K ? w[(int64_t)t * K + lane] : 0.0f;
+  int pk[KMAX];
+  float wk[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    pk[k] = __builtin_amdgcn_readlane(my_pos, k);
+    wk[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k));
+  }
+  u32x4* dst = out + (int64_t)t * V;
+  for (int v0 = 0; v0 < V; v0 += kWave * U) {
+    u32x4 r[KMAX][U];
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      if (pk[k] >= 0) {
+        const u32x4* row = y + (int64_t)pk[k] * V;
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const int idx = v0 + u * kWave + lane;
+          if (idx < V) r[k][u] = row[idx];
+        }
+      }
+    }
+    float acc[U][8];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      if (pk[k] >= 0) {
+        const float wt = wk[k];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+          const uint32_t v4[4] = {r[k][u].x, r[k][u].y, r[k][u].z, r[k][u].w};
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            acc[u][2 * i] = __builtin_fmaf(wt, bf16lo(v4[i]), acc[u][2 * i]);
+            acc[u][2 * i + 1] = __builtin_fmaf(wt, bf16hi(v4[i]), acc[u][2 * i + 1]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int idx = v0 + u * kWave + lane;
+      if (idx < V) {
+        u32x4 o;
+        o.x = f32_to_bf16_rne(acc[u][0]) | (f32_to_bf16_rne(acc[u][1]) << 16);
+        o.y = f32_to_bf16_rne(acc[u][2]) | (f32_to_bf16_rne(acc[u][3]) << 16);
+        o.z = f32_to_bf16_rne(acc[u][4]) | (f32_to_bf16_rne(acc[u][5]) << 16);
+        o.w = f32_to_bf16_rne(acc[u][6]) | (f32_to_bf16_rne(acc[u][7]) << 16);
+        __builtin_nontemporal_store(o, dst + idx);
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// 1-D uneven all_to_all_single (test_make_a2a_exchange_plan / allToAllGet on
+// the PyTorch compare view; aws-neuron/torch-neuronx PR #1035).
+// ---------------------------------------------------------------------------
+constexpr int kSplitsPlanThreads = 64;
+
+__global__ __launch_bounds__(kSplitsPlanThreads) void plan_splits_kernel(
+    int W, const int64_t* __restrict__ in_splits, int64_t* __restrict__ src_offsets,
+    int64_t* __restrict__ out_splits, int64_t* __restrict__ dst_offsets,
+    int64_t* __restrict__ rank_offsets) {
+  __shared__ int64_t recv[kSplitsPlanThreads];
+  const int r = threadIdx.x;  // receiver
+  if (r < W) {
+    int64_t run = 0;
+    for (int p = 0; p < W; ++p) {
+      const int64_t n = in_splits[(int64_t)p * W + r];
+      out_splits[(int64_t)r * W + p] = n;
+      dst_offsets[(int64_t)r * W + p] = run;
+      run += n;
+      int64_t so = 0;
+      for (int r2 = 0; r2 < r; ++r2) so += in_splits[(int64_t)p * W + r2];
+      src_offsets[(int64_t)r * W + p] = so;
+    }
+    recv[r] = run;
+  }
+  __syncthreads();
+  if (r == 0) {
+    int64_t run = 0;
+    for (int i = 0; i < W; ++i) {
+      rank_offsets[i] = run;
+      run += recv[i];
+    }
+    rank_offsets[W] = run;
+  }
+}
+
+// Grid: x = chunk q = r * W + p (receiver r, sender p), y = blocks per chunk.
+// Each wave copies whole rows of its chunk, 16-byte vectors, U per lane.
+template <int U>
+__global__ __launch_bounds__(kRowThreads) void copy_splits_kernel(
+    const u32x4* __restrict__ in, u32x4* __restrict__ out, const int64_t* __restrict__ src_offsets,
+    const int64_t* __restrict__ out_splits, const int64_t* __restrict__ dst_offsets,
+    const int64_t* __restrict__ rank_offsets, int W, int64_t R, int64_t Vr) {
+  const int q = blockIdx.x;
+  const int r = q / W, p = q - r * W;
+  const int64_t n = out_splits[q];
+  const int64_t src = src_offsets[q];
+  const int64_t dst = rank_offsets[r] + dst_offsets[q];
+  if (n == 0) return;
+  if (n < 0 || src < 0 || src + n > R || dst < 0 || dst + n > (int64_t)W * R) {
+    if (blockIdx.y == 0 && threadIdx.x == 0) raise_device_error(kErrSplits);
+    return;
+  }
+  const int lane = lane_id();
+  const int64_t step = (int64_t)gridDim.y * kTokensPerBlock;
+  for (int64_t i = (int64_t)blockIdx.y * kTokensPerBlock + threadIdx.x / kWave; i < n; i += step) {
+    const u32x4* s = in + ((int64_t)p * R + src + i) * Vr;
+    u32x4* d = out + (dst + i) * Vr;
+    for (int64_t v0 = 0; v0 < Vr; v0 += kWave * U) {
+      u32x4 t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t idx = v0 + u * kWave + lane;
+        if (idx < Vr) t[u] = s[idx];
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t idx = v0 + u * kWave + lane;
+        if (idx < Vr) __builtin_nontemporal_store(t[u], d + idx);
+      }
+    }
+  }
+}
+
+}  // namespace ep

@@ -1,0 +1,197 @@
+/*
+ * ep_mi355x.h -- C ABI of the MI355X (gfx950) MoE expert-parallel dispatch /
+ * combine library (libep_mi355x.so).
+ *
+ * The W expert-parallel ranks are regions of one GPU's memory.  A token t
+ * belongs to source rank s = t / Tw (Tw = T / W, each rank owns the same
+ * number of tokens, as the global batch of the Huawei CANN
+ * "aclnnMoeDistributeDispatchV2" page is Bs * epWorldSize); expert e lives on
+ * rank d = e / ne (ne = E / W, the expert-to-rank mapping of
+ * _allToAllV_2d_index_push_kernel on the PyTorch compare view
+ * "ciflow/h100-symm-mem/166772").
+ *
+ * Conventions for every entry point:
+ *  - Array arguments are DEVICE pointers owned by the caller, row-major and
+ *    contiguous.  The library never allocates, never synchronises (except
+ *    ep_device_error) and never reads device data on the host.
+ *  - bf16 values travel as uint16_t bit patterns, E4M3FN fp8 values as
+ *    uint8_t codes.
+ *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *    call only enqueues work on it; outputs are ready when the stream
+ *    reaches that point.
+ *  - Return value: an ep_status.  Argument checks happen on the host before
+ *    anything is enqueued; on a non-OK return nothing was enqueued and
+ *    ep_last_error() describes the first failed check (thread-local).
+ *    Status classes follow the page above's return codes: null pointer,
+ *    invalid value / dtype, unsupported shape.
+ *  - Data errors that only the device can see (an expert id outside [0, E)
+ *    on a live copy, a 1-D plan that names rows outside a rank's input) do
+ *    not abort: the offending copy is dropped and a bit is set in the
+ *    device error word, read with ep_device_error().
+ *  - Outputs must not overlap inputs (no aliasing), as the all-gather-add
+ *    contract of ROCm/aiter PR #6960 requires.
+ */
+#ifndef EP_MI355X_H
+#define EP_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    EP_OK = 0,
+    EP_ERR_NULLPTR = 1,     /* a required pointer is NULL                  */
+    EP_ERR_INVALID = 2,     /* bad value, alignment, aliasing or dtype     */
+    EP_ERR_UNSUPPORTED = 3, /* shape outside the supported limits          */
+    EP_ERR_WORKSPACE = 4,   /* workspace too small or not 256-byte aligned */
+    EP_ERR_HIP = 5          /* the HIP runtime refused a launch            */
+} ep_status;
+
+typedef enum {
+    EP_BF16 = 0,       /* expandX rows are bf16, bit copies of x           */
+    EP_FP8_E4M3FN = 1  /* expandX rows are OCP E4M3FN codes + fp32 scales  */
+} ep_dtype;
+
+/* Device error bits (ep_device_error). */
+#define EP_DEVERR_BAD_EXPERT 1 /* a live copy named an expert outside [0,E) */
+#define EP_DEVERR_SPLITS 2     /* a 1-D plan named rows outside the buffers */
+#define EP_DEVERR_PLAN_STALL 4 /* the plan's look-back waited too long (the
+                                  workspace was not initialised): plan invalid */
+#define EP_DEVERR_BAD_ROW 8    /* dispatch/combine met a pos >= cap_rows: that
+                                  copy was skipped */
+
+/* Limits: 1 <= K <= 16 and 1 <= E <= 1024 (the dispatch page's top-K and
+ * expert-count limits), W >= 1, W divides E and T, T * K < 2^31,
+ * H % 8 == 0 for bf16 rows and H % 16 == 0 for fp8 rows (16-byte vectors),
+ * H <= 65536. */
+#define EP_MAX_K 16
+#define EP_MAX_E 1024
+#define EP_MAX_H 65536
+#define EP_MAX_SPLITS_W 64
+
+/* Device outputs of ep_plan.  Every pointer except `occ` is required.
+ * Sources: the 2-D exchange plan (make2dExchangePlan and
+ * test_make_a2a_2d_exchange_plan on the PyTorch compare view
+ * "ciflow/h100-symm-mem/166772"), get_occurrence_numbers on the same page,
+ * expertTokenNumsOut / epRecvCountsOut on the CANN dispatch page. */
+typedef struct {
+    int64_t *in_splits;      /* [W][E] live copies from source rank s to expert e     */
+    int64_t *src_offsets;    /* [W][E] exclusive scan of in_splits[s][:] over e       */
+    int64_t *out_splits;     /* [W][E/W][W] out_splits[d][le][s] = in_splits[s][d*ne+le] */
+    int64_t *dst_offsets;    /* [W][E] row of (s, e)'s chunk inside rank e/ne's buffer:
+                                sum_{s'<s} in_splits[s'][e]
+                                + sum_{le'<le} expert_counts[d*ne+le']                  */
+    int64_t *expert_counts;  /* [E] rows each expert receives                          */
+    int64_t *expert_offsets; /* [E] exclusive scan of expert_counts (global row start) */
+    int64_t *rank_offsets;   /* [W+1] global row where rank d's region starts;
+                                rank_offsets[W] = N, the number of live copies         */
+    int32_t *pos;            /* [T][K] global expandX row of copy (t,k), -1 if not live */
+    int32_t *occ;            /* [T][K] 0-based occurrence inside the (source rank,
+                                expert) bucket in flattened (t,k) order, -1 if not
+                                live; may be NULL                                      */
+} ep_plan_t;
+
+/* Returns 1 if ep_plan / ep_dispatch / ep_combine accept these dimensions
+ * and this row dtype, else 0.  Never fails, never touches the GPU (the
+ * availability predicate of ROCm/aiter PR #6960's
+ * should_custom_ag_lastdim_add). */
+int ep_supported(int32_t T, int32_t K, int32_t E, int32_t W, int32_t H, int32_t out_dtype);
+
+/* Bytes of device workspace ep_plan needs for these dimensions (the
+ * two-phase GetWorkspaceSize convention of the CANN dispatch page).
+ * Returns 0 for dimensions ep_supported rejects. */
+size_t ep_workspace_size(int32_t T, int32_t K, int32_t E, int32_t W);
+
+/* Puts a fresh workspace into its initial state (enqueues one fill kernel
+ * on `stream`).  Call once after allocating it; ep_plan leaves the
+ * workspace in the same state for the next call.  `workspace` must be
+ * 256-byte aligned. */
+int ep_workspace_init(void *workspace, size_t ws_bytes, void *stream);
+
+/* Exchange plan, stable occurrences and positions.
+ *   topk_ids [T][K] int32: top-K expert ids (CANN expertIds is INT32).
+ *   active   [T] uint8 or NULL: token t takes part iff active[t] != 0
+ *            (xActiveMaskOptional, any 1-D pattern accepted).
+ *   plan     device output arrays, see ep_plan_t.
+ * A copy (t,k) is live iff its token is active and 0 <= id < E.
+ * pos[t][k] = rank_offsets[d] + dst_offsets[s][e] + occ[t][k]: expandX is
+ * grouped by destination rank, then local expert, then source rank, then
+ * flattened (t,k) order -- the row an index-push puts copy (t,k) to
+ * (_allToAllV_2d_index_push_kernel: dst_offsets[expert] + occurrence).
+ * The result is deterministic and identical to the serial definition.
+ * T == 0 writes the all-zero plan.  The workspace (size from
+ * ep_workspace_size, initialised once with ep_workspace_init) must not be
+ * used by two calls in flight at the same time. */
+int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t *topk_ids,
+            const uint8_t *active, const ep_plan_t *plan, void *workspace,
+            size_t ws_bytes, void *stream);
+
+/* Dispatch scatter: for every copy with pos[t][k] >= 0,
+ *   EP_BF16:       expand_x[pos][:] = x[t][:]  (bit copy, H bf16 = 2H bytes)
+ *   EP_FP8_E4M3FN: per-token dynamic quantisation (CANN quantMode 2):
+ *                  amax = max_h |x[t][h]|, scale = fl32(amax / 448),
+ *                  expand_x[pos][h] = E4M3FN_rne_sat(fl32(x[t][h] / scale))
+ *                  (all codes 0x00 when scale == 0), expand_scales[pos] = scale
+ *                  (dynamicScalesOut: one fp32 scale per expanded row).
+ * x [T][H] bf16; expand_x [cap_rows][H] (uint16 bf16 or uint8 codes);
+ * expand_scales [cap_rows] fp32, required for fp8, ignored for bf16.
+ * cap_rows >= T*K (the worst case: every copy live).  Rows no copy names
+ * are not written.  x, expand_x 16-byte aligned; T == 0 enqueues nothing. */
+int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t *x, const int32_t *pos,
+                int32_t out_dtype, void *expand_x, float *expand_scales, int64_t cap_rows,
+                void *stream);
+
+/* Weighted combine: for every token t and column h,
+ *   out[t][h] = bf16_rne( sum over k = 0..K-1 with pos[t][k] >= 0 of
+ *                         w[t][k] * y[pos[t][k]][h] )
+ * accumulated in fp32 with one fused multiply-add per k in increasing k,
+ * starting from +0 (a token with no live copy gets a +0 row; a copy with
+ * pos -1 contributes nothing, as a routed index of -1 with weight 0 in the
+ * MoE-finalize pattern of flashinfer PR #4358).  y [cap_rows][H] bf16 (the
+ * expert outputs in expandX layout), weights [T][K] fp32 gate scales
+ * (expertScalesOptional), out [T][H] bf16.  y, out 16-byte aligned; every
+ * pos must be < cap_rows (ep_plan guarantees it). */
+int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t *y, int64_t cap_rows,
+               const int32_t *pos, const float *weights, uint16_t *out, void *stream);
+
+/* 1-D uneven all_to_all_single plan (test_make_a2a_exchange_plan on the
+ * PyTorch compare view; the uneven-split lowering of aws-neuron/torch-neuronx
+ * PR #1035).  in_splits[p][r] = rows rank p sends to rank r.  Outputs,
+ * receiver-indexed, all [W][W] except rank_offsets [W+1]:
+ *   out_splits[r][p]  = in_splits[p][r]
+ *   src_offsets[r][p] = sum_{r'<r} in_splits[p][r']  (row in p's input)
+ *   dst_offsets[r][p] = sum_{p'<p} out_splits[r][p'] (row in r's output)
+ *   rank_offsets[r]   = rows received by ranks < r; [W] = total rows.
+ * 1 <= W <= EP_MAX_SPLITS_W.  One workgroup, enqueued on `stream`. */
+int ep_plan_splits(int32_t W, const int64_t *in_splits, int64_t *src_offsets,
+                   int64_t *out_splits, int64_t *dst_offsets, int64_t *rank_offsets,
+                   void *stream);
+
+/* 1-D uneven all-to-all data move (allToAllGet on the PyTorch compare view):
+ * for every receiver r and sender p, rows
+ *   in[p][src_offsets[r][p] + i]  ->  out[rank_offsets[r] + dst_offsets[r][p] + i]
+ * for i < out_splits[r][p].  in [W][R] rows, out [W*R] rows (the packed
+ * receive buffers of all ranks), each row `stride_bytes` long (multiple of
+ * 16; in, out 16-byte aligned).  A chunk that would read past row R of its
+ * sender or write past row W*R is skipped and sets EP_DEVERR_SPLITS. */
+int ep_dispatch_splits(int32_t W, int64_t R, int64_t stride_bytes, const void *in,
+                       const int64_t *src_offsets, const int64_t *out_splits,
+                       const int64_t *dst_offsets, const int64_t *rank_offsets, void *out,
+                       void *stream);
+
+/* Thread-local description of the last non-OK status ("" if none). */
+const char *ep_last_error(void);
+
+/* Synchronises `stream`, then returns in *code the device error bits
+ * (EP_DEVERR_*) raised on the current device since the previous call, and
+ * clears them. */
+int ep_device_error(void *stream, int32_t *code);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* EP_MI355X_H */

@@ -1,0 +1,167 @@
+"""Host-only checks of the C ABI (no GPU needed, nothing is launched).
+
+* libep_mi355x.so loads and exports every function include/*.h declares.
+* ep_supported / ep_workspace_size follow the documented limits.
+* Every argument check fails on the host with the documented status before
+  anything is enqueued: NULL pointers, misalignment, aliasing outputs,
+  unsupported dimensions, a too-small capacity or workspace.  The checks
+  mirror the validation contract of ROCm/aiter PR #6960 and the status classes
+  of the CANN aclnnMoeDistributeDispatchV2 return codes.
+* An empty input (T == 0, R == 0) returns EP_OK without launching.
+"""
+import ctypes
+import glob
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def ep():
+    from combine_ep_plan_02_amd import build
+    if build.is_stale():
+        build.build()
+    import combine_ep_plan_02_amd as ep
+    return ep
+
+
+def declared_functions():
+    names = set()
+    for h in glob.glob(os.path.join(ROOT, "include", "*.h")):
+        text = open(h).read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        names |= set(re.findall(r"^[A-Za-z_][\w\s\*]*?\b(ep_\w+)\s*\(", text, flags=re.M))
+    return sorted(names)
+
+
+def test_library_exports_every_declared_symbol(ep):
+    names = declared_functions()
+    assert len(names) >= 10, names
+    lib = ctypes.CDLL(ep.library_path())
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in include/ but not exported"
+    assert set(names) == set(ep.EXPORTED)
+
+
+def test_supported_predicate(ep):
+    assert ep.ep_supported(64, 2, 8, 2, 128, ep.EP_BF16)
+    assert ep.ep_supported(16384, 8, 256, 32, 7168, ep.EP_FP8_E4M3FN)
+    assert ep.ep_supported(0, 1, 1, 1, 8, ep.EP_BF16)
+    assert not ep.ep_supported(64, 17, 8, 2, 128, ep.EP_BF16)      # K > 16
+    assert not ep.ep_supported(64, 2, 1025, 1, 128, ep.EP_BF16)    # E > 1024
+    assert not ep.ep_supported(64, 2, 9, 2, 128, ep.EP_BF16)       # W does not divide E
+    assert not ep.ep_supported(63, 2, 8, 2, 128, ep.EP_BF16)       # W does not divide T
+    assert not ep.ep_supported(64, 2, 8, 2, 132, ep.EP_BF16)       # H % 8
+    assert not ep.ep_supported(64, 2, 8, 2, 136, ep.EP_FP8_E4M3FN)  # H % 16
+    assert not ep.ep_supported(64, 2, 8, 2, 128, 7)                # unknown dtype
+    assert not ep.ep_supported(1 << 28, 16, 8, 2, 128, ep.EP_BF16)  # T*K >= 2^31
+
+
+def test_workspace_size(ep):
+    assert ep.ep_workspace_size(64, 2, 8, 2) > 0
+    assert ep.ep_workspace_size(64, 2, 8, 2) % 256 == 0
+    assert ep.ep_workspace_size(0, 2, 8, 2) == 256
+    assert ep.ep_workspace_size(64, 17, 8, 2) == 0
+    big = ep.ep_workspace_size(16384, 8, 256, 32)
+    small = ep.ep_workspace_size(64, 8, 256, 32)
+    assert big > small
+
+
+# Fake device addresses: the checks never dereference them.
+A = 1 << 40
+
+
+def plan_struct(ep, base=A, skip=()):
+    s = ep._PlanT()
+    for i, (f, _) in enumerate(ep._PlanT._fields_):
+        setattr(s, f, None if f in skip else base + (i + 1) * (1 << 30))
+    return s
+
+
+def call_plan(ep, T=64, K=2, E=8, W=2, ids=A, active=None, st=None, ws=A + (1 << 36),
+              ws_bytes=1 << 20):
+    st = st if st is not None else plan_struct(ep)
+    rc = ep.lib.ep_plan(T, K, E, W, ids, active, ctypes.byref(st), ws, ws_bytes, None)
+    return rc, ep.lib.ep_last_error().decode()
+
+
+def test_plan_rejections(ep):
+    assert call_plan(ep, K=0)[0] == ep.EP_ERR_UNSUPPORTED
+    assert call_plan(ep, K=17)[0] == ep.EP_ERR_UNSUPPORTED
+    assert call_plan(ep, E=9)[0] == ep.EP_ERR_UNSUPPORTED
+    assert call_plan(ep, T=63)[0] == ep.EP_ERR_UNSUPPORTED
+    assert call_plan(ep, T=-2)[0] == ep.EP_ERR_INVALID
+    assert call_plan(ep, ids=None)[0] == ep.EP_ERR_NULLPTR
+    assert call_plan(ep, st=plan_struct(ep, skip=("pos",)))[0] == ep.EP_ERR_NULLPTR
+    assert call_plan(ep, st=plan_struct(ep, skip=("rank_offsets",)))[0] == ep.EP_ERR_NULLPTR
+    assert call_plan(ep, ws=None)[0] == ep.EP_ERR_NULLPTR
+    assert call_plan(ep, ws=A + 8)[0] == ep.EP_ERR_WORKSPACE          # not 256-aligned
+    assert call_plan(ep, ws_bytes=16)[0] == ep.EP_ERR_WORKSPACE       # too small
+    assert call_plan(ep, ids=A + 2)[0] == ep.EP_ERR_INVALID           # misaligned ids
+    st = plan_struct(ep)
+    st.pos = A   # pos aliases topk_ids
+    rc, msg = call_plan(ep, st=st)
+    assert rc == ep.EP_ERR_INVALID and "overlaps" in msg
+    st = plan_struct(ep)
+    st.in_splits = st.src_offsets   # two outputs share memory
+    assert call_plan(ep, st=st)[0] == ep.EP_ERR_INVALID
+    assert ep.lib.ep_plan(64, 2, 8, 2, A, None, None, A, 1 << 20, None) == ep.EP_ERR_NULLPTR
+
+
+def test_dispatch_rejections(ep):
+    d = ep.lib.ep_dispatch
+    X, P, EX, S = A, A + (1 << 34), A + (1 << 35), A + (1 << 36)
+    assert d(64, 2, 128, X, P, ep.EP_BF16, EX, None, 127, None) == ep.EP_ERR_INVALID  # cap < T*K
+    assert d(64, 2, 132, X, P, ep.EP_BF16, EX, None, 128, None) == ep.EP_ERR_UNSUPPORTED
+    assert d(64, 2, 136, X, P, ep.EP_FP8_E4M3FN, EX, S, 128, None) == ep.EP_ERR_UNSUPPORTED
+    assert d(64, 2, 128, X, P, 5, EX, None, 128, None) == ep.EP_ERR_INVALID
+    assert d(64, 2, 128, None, P, ep.EP_BF16, EX, None, 128, None) == ep.EP_ERR_NULLPTR
+    assert d(64, 2, 128, X, P, ep.EP_FP8_E4M3FN, EX, None, 128, None) == ep.EP_ERR_NULLPTR
+    assert d(64, 2, 128, X + 8, P, ep.EP_BF16, EX, None, 128, None) == ep.EP_ERR_INVALID
+    assert d(64, 2, 128, X, P, ep.EP_BF16, X + 256, None, 128, None) == ep.EP_ERR_INVALID  # alias
+    assert d(64, 2, 128, X, P, ep.EP_FP8_E4M3FN, EX, EX + 64, 128, None) == ep.EP_ERR_INVALID
+    assert d(64, 0, 128, X, P, ep.EP_BF16, EX, None, 128, None) == ep.EP_ERR_UNSUPPORTED
+    # empty input: OK, nothing enqueued, pointers may be NULL
+    assert d(0, 2, 128, None, None, ep.EP_BF16, None, None, 0, None) == ep.EP_OK
+
+
+def test_combine_rejections(ep):
+    c = ep.lib.ep_combine
+    Y, P, Wt, O = A, A + (1 << 34), A + (1 << 35), A + (1 << 36)
+    assert c(64, 2, 132, Y, 128, P, Wt, O, None) == ep.EP_ERR_UNSUPPORTED
+    assert c(64, 2, 128, None, 128, P, Wt, O, None) == ep.EP_ERR_NULLPTR
+    assert c(64, 2, 128, Y, 128, P, None, O, None) == ep.EP_ERR_NULLPTR
+    assert c(64, 2, 128, Y, 128, P + 2, Wt, O, None) == ep.EP_ERR_INVALID
+    assert c(64, 2, 128, Y, 128, P, Wt, Y + 1024, None) == ep.EP_ERR_INVALID  # out aliases y
+    assert c(64, 2, 128, Y, -1, P, Wt, O, None) == ep.EP_ERR_INVALID
+    assert c(0, 2, 128, None, 0, None, None, None, None) == ep.EP_OK
+    msg = (c(64, 2, 128, Y, 128, P, Wt, Y + 1024, None), ep.lib.ep_last_error().decode())[1]
+    assert "overlaps" in msg
+
+
+def test_splits_rejections(ep):
+    p = ep.lib.ep_plan_splits
+    B = [A + i * (1 << 30) for i in range(5)]
+    assert p(0, *B, None) == ep.EP_ERR_UNSUPPORTED
+    assert p(65, *B, None) == ep.EP_ERR_UNSUPPORTED
+    assert p(8, B[0], None, B[2], B[3], B[4], None) == ep.EP_ERR_NULLPTR
+    assert p(8, B[0], B[0] + 8, B[2], B[3], B[4], None) == ep.EP_ERR_INVALID  # overlap
+    assert p(8, B[0] + 4, B[1], B[2], B[3], B[4], None) == ep.EP_ERR_INVALID  # misaligned
+    d = ep.lib.ep_dispatch_splits
+    IN, OUT = A + (1 << 36), A + (1 << 37)
+    assert d(8, 16, 24, IN, *B[1:], OUT, None) == ep.EP_ERR_UNSUPPORTED    # stride % 16
+    assert d(8, -1, 32, IN, *B[1:], OUT, None) == ep.EP_ERR_INVALID
+    assert d(8, 16, 32, IN, *B[1:], IN + 16, None) == ep.EP_ERR_INVALID   # out aliases in
+    assert d(8, 16, 32, None, *B[1:], OUT, None) == ep.EP_ERR_NULLPTR
+    assert d(8, 0, 32, None, None, None, None, None, None, None) == ep.EP_OK
+
+
+def test_last_error_is_cleared_by_predicates(ep):
+    call_plan(ep, K=0)
+    before = ep.lib.ep_last_error().decode()
+    assert "K must be" in before
+    ep.ep_supported(64, 2, 8, 2, 128)
+    assert ep.lib.ep_last_error().decode() == before  # the predicate never clobbers it

@@ -1,0 +1,313 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Plan, positions, occurrences, bf16 and fp8 dispatch are compared bit for bit;
+the combine within 1 bf16 ulp (it is expected to be bit-exact: both sides use
+one fp32 fused multiply-add per k in increasing k).  Small cases run the
+oracle on the whole input; the full-size workloads (in the launch
+configuration the benchmark times) compare the whole plan and sampled tokens.
+"""
+import numpy as np
+import pytest
+import torch
+
+import combine_ep_plan_02_amd as ep
+import oracle
+import workloads
+from _gpu_util import GpuRun, assert_plan_equal, bf16_ulp_distance, dev, host
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+@pytest.fixture(autouse=True)
+def _clear_device_errors():
+    torch.cuda.synchronize()
+    ep.ep_device_error()
+    yield
+
+
+def random_case(T, K, E, W, mask_frac, seed, routing="dup"):
+    rng = np.random.default_rng(seed)
+    if routing == "dup":
+        ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    elif routing == "distinct":
+        ids = workloads.routing_uniform(rng, T, E, K)
+    elif routing == "zipf":
+        ids = workloads.routing_zipf(rng, T, E, K, 1.2, min(16, E - K))
+    else:
+        raise ValueError(routing)
+    active = (rng.random(T) >= mask_frac).astype(np.uint8) if mask_frac > 0 else None
+    return ids, active
+
+
+PLAN_CASES = [
+    # T, K, E, W, mask, seed, routing       what it stresses
+    (64, 2, 8, 2, 0.0, 0, "distinct"),      # config-0 shape
+    (3000, 5, 60, 6, 0.3, 1, "dup"),        # ragged tiles: Tw=500 -> 409 + 91 tokens
+    (64, 16, 1024, 4, 0.0, 2, "distinct"),  # largest K and E
+    (4096, 1, 1, 1, 0.5, 3, "dup"),         # E = 1, K = 1, one rank
+    (1024, 8, 256, 8, 0.25, 4, "zipf"),     # skew, empty experts, mask
+    (6144, 3, 48, 48, 0.1, 5, "dup"),       # one expert per rank, 48 ranks
+    (512, 4, 4, 2, 0.0, 6, "dup"),          # heavy duplicates in a wave
+    (8, 3, 6, 2, 0.0, 7, "dup"),            # tile smaller than a wave
+    (20000, 7, 14, 2, 0.2, 8, "dup"),       # 2 ranks x 35 tiles, long look-back
+]
+
+
+@pytest.mark.parametrize("case", PLAN_CASES, ids=[f"T{c[0]}K{c[1]}E{c[2]}W{c[3]}" for c in PLAN_CASES])
+def test_plan_parity(case):
+    T, K, E, W, mask, seed, routing = case
+    say("plan case", case)
+    ids, active = random_case(T, K, E, W, mask, seed, routing)
+    want = oracle.plan(ids, E, W, active)
+    g = GpuRun(ids, E, W, active)
+    g.run_plan()
+    assert_plan_equal(g.plan_host(), want)
+    assert ep.ep_device_error() == 0
+
+
+def test_plan_empty_tokens():
+    say("plan T=0")
+    ids = np.zeros((0, 4), np.int32)
+    g = GpuRun(ids, 8, 2)
+    for f in ("in_splits", "expert_counts", "rank_offsets"):
+        getattr(g.plan, f).fill_(-7)
+    g.run_plan()
+    want = oracle.plan(ids, 8, 2)
+    assert_plan_equal(g.plan_host(), want)
+
+
+def test_plan_invalid_ids_are_dropped_and_flagged():
+    say("plan invalid ids")
+    rng = np.random.default_rng(9)
+    T, K, E, W = 256, 4, 16, 4
+    ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    ids[3, 1] = -1
+    ids[100, 0] = E
+    ids[200, 3] = 1 << 30
+    active = np.ones(T, np.uint8)
+    active[200] = 0          # an inactive token's bad id is not an error by itself
+    want = oracle.plan(ids, E, W, active)
+    g = GpuRun(ids, E, W, active)
+    g.run_plan()
+    assert_plan_equal(g.plan_host(), want)
+    assert ep.ep_device_error() == ep.EP_DEVERR_BAD_EXPERT == want.err
+
+
+def test_plan_reuse_and_determinism():
+    say("plan reuse")
+    ids, active = random_case(3000, 5, 60, 6, 0.3, 1)
+    g = GpuRun(ids, 60, 6, active)
+    first = None
+    for _ in range(3):  # the workspace is left ready for the next call
+        g.run_plan()
+        cur = g.plan_host()
+        if first is None:
+            first = cur
+        for k in cur:
+            assert (cur[k] == first[k]).all(), k
+    assert_plan_equal(first, oracle.plan(ids, 60, 6, active))
+
+
+@pytest.mark.parametrize("H", [8, 128, 264, 1032, 4104, 7168])
+def test_dispatch_bf16_and_combine_parity(H):
+    T, K, E, W = 96, 5, 20, 4
+    say("dispatch/combine bf16 H", H)
+    cfg = workloads.MoEConfig("t", T=T, H=H, E=E, K=K, W=W, mask_frac=0.2, seed=H)
+    inp = workloads.moe_inputs(cfg)
+    p = oracle.plan(inp.ids, E, W, inp.active)
+    cap = cfg.cap_rows
+    g = GpuRun(inp.ids, E, W, inp.active)
+    g.run_plan()
+    x = dev(inp.x)
+    ex = torch.full((cap, H), 0x5A5A, dtype=torch.int16, device="cuda")  # sentinel rows
+    ep.ep_dispatch(x, g.plan.pos, ex)
+    want_ex = oracle.dispatch_bf16(inp.x, p.pos, cap, fill=0x5A5A)
+    assert (host(ex, np.uint16) == want_ex).all()
+    # combine the dispatched rows back, with the gate weights
+    w = dev(inp.weights)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ep.ep_combine(ex, g.plan.pos, w, out)
+    want = oracle.combine(want_ex, p.pos, inp.weights)
+    d = bf16_ulp_distance(host(out, np.uint16), want)
+    assert d.max() <= 1, d.max()
+    assert (d == 0).all(), f"{int((d > 0).sum())} elements 1 ulp apart"
+
+
+@pytest.mark.parametrize("K", [1, 3, 4, 8, 11, 16])
+def test_combine_parity_random_rows(K):
+    T, H, E, W = 80, 520, 32, 4
+    say("combine K", K)
+    cfg = workloads.MoEConfig("t", T=T, H=H, E=E, K=K, W=W, mask_frac=0.1, seed=50 + K)
+    inp = workloads.moe_inputs(cfg, with_x=False)
+    p = oracle.plan(inp.ids, E, W, inp.active)
+    y = workloads.expert_outputs(cfg.cap_rows, H, seed=K)
+    w = inp.weights * np.float32(1.7)
+    g = GpuRun(inp.ids, E, W, inp.active)
+    g.run_plan()
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ep.ep_combine(dev(y), g.plan.pos, dev(w), out)
+    want = oracle.combine(y, p.pos, w)
+    d = bf16_ulp_distance(host(out, np.uint16), want)
+    assert d.max() <= 1
+    assert (d == 0).all()
+
+
+def test_combine_closed_forms():
+    say("combine closed forms")
+    # unit weights on the dispatched rows: bf16(K_live * x), exact in fp32
+    T, H, E, W, K = 64, 256, 8, 2, 6
+    cfg = workloads.MoEConfig("t", T=T, H=H, E=E, K=K, W=W, mask_frac=0.25, seed=3)
+    inp = workloads.moe_inputs(cfg)
+    g = GpuRun(inp.ids, E, W, inp.active)
+    g.run_plan()
+    ex = torch.zeros((cfg.cap_rows, H), dtype=torch.int16, device="cuda")
+    ep.ep_dispatch(dev(inp.x), g.plan.pos, ex)
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ep.ep_combine(ex, g.plan.pos, torch.ones((T, K), dtype=torch.float32, device="cuda"), out)
+    k_live = (host(g.plan.pos) >= 0).sum(axis=1)
+    xf = (inp.x.astype(np.uint32) << 16).view(np.float32)
+    exact = (xf * k_live[:, None].astype(np.float32)) + np.float32(0.0)
+    assert (host(out, np.uint16) == workloads.bf16_bits_from_f32(exact)).all()
+    # association probe: rows 2^24, 1, -2^24 summed in k order give 0
+    y = workloads.bf16_bits_from_f32(np.repeat(np.array([[2.0 ** 24], [1.0], [-(2.0 ** 24)]], np.float32), 8, 1))
+    o1 = torch.empty((1, 8), dtype=torch.int16, device="cuda")
+    ep.ep_combine(dev(y), dev(np.array([[0, 1, 2]], np.int32)), dev(np.ones((1, 3), np.float32)), o1)
+    assert (host(o1, np.uint16) == 0).all()
+    ep.ep_combine(dev(y), dev(np.array([[0, 2, 1]], np.int32)), dev(np.ones((1, 3), np.float32)), o1)
+    assert (host(o1, np.uint16) == 0x3F80).all()  # 1.0
+
+
+FP8_H = [16, 272, 2048, 7168, 9216]
+
+
+@pytest.mark.parametrize("H", FP8_H)
+def test_dispatch_fp8_parity(H):
+    T, K, E, W = 64, 4, 16, 4
+    say("dispatch fp8 H", H)
+    cfg = workloads.MoEConfig("t", T=T, H=H, E=E, K=K, W=W, sigma=3.0, mask_frac=0.25, seed=H)
+    inp = workloads.moe_inputs(cfg)
+    x = inp.x.copy()
+    act = inp.active if inp.active is not None else np.ones(T, np.uint8)
+    act[:6] = 1
+    x[0] = 0                                                              # amax == 0
+    x[1] = workloads.bf16_bits_from_f32(np.full(H, 1e-39, np.float32))    # subnormal bf16
+    x[2] = workloads.bf16_bits_from_f32(np.linspace(-3e38, 3e38, H, dtype=np.float32))
+    x[3, :] = 0x8000                                                      # all -0
+    x[4] = workloads.bf16_bits_from_f32((np.arange(H) % 17 - 8).astype(np.float32) * np.float32(0.0625))
+    x[5] = workloads.bf16_bits_from_f32(np.ldexp(np.ones(H, np.float32), (np.arange(H) % 40) - 30))
+    p = oracle.plan(inp.ids, E, W, act)
+    cap = cfg.cap_rows
+    want_q, want_s = oracle.dispatch_fp8(x, p.pos, cap, fill_q=0xA5, fill_scale=-2.0)
+    g = GpuRun(inp.ids, E, W, act)
+    g.run_plan()
+    q = torch.full((cap, H), 0xA5, dtype=torch.uint8, device="cuda")
+    sc = torch.full((cap,), -2.0, dtype=torch.float32, device="cuda")
+    ep.ep_dispatch(dev(x), g.plan.pos, q, sc, out_dtype=ep.EP_FP8_E4M3FN)
+    got_q, got_s = host(q), host(sc)
+    bad = np.argwhere(got_q != want_q)
+    assert bad.size == 0, f"{len(bad)} codes differ, first {bad[0].tolist()}: got {got_q[tuple(bad[0])]:#x} want {want_q[tuple(bad[0])]:#x}"
+    assert (got_s.view(np.uint32) == want_s.view(np.uint32)).all()
+
+
+def test_fp8_encoder_exhaustive_over_quotients():
+    """Every fp32 quotient class the encoder can see: drive it with x / scale
+    where scale = 1 (amax 448) and x spans every bf16 pattern of magnitude
+    <= 448, plus the rounding boundaries."""
+    say("fp8 encoder sweep")
+    mags = np.arange(0, 0x43E1, dtype=np.uint16)            # bf16 magnitudes 0 .. 448
+    vals = np.concatenate([mags, mags | 0x8000])
+    H = 16 * ((vals.size + 15) // 16)
+    row = np.zeros(H, np.uint16)
+    row[: vals.size] = vals
+    row[-1] = 0x43E0                                        # 448: amax, so scale = 1
+    T, K = 1, 1
+    x = row.reshape(1, H)
+    pos = np.zeros((1, 1), np.int32)
+    want_q, want_s = oracle.dispatch_fp8(x, pos, 1)
+    q = torch.zeros((1, H), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((1,), dtype=torch.float32, device="cuda")
+    ep.ep_dispatch(dev(x), dev(pos), q, sc, out_dtype=ep.EP_FP8_E4M3FN)
+    assert float(host(sc)[0]) == 1.0 == float(want_s[0])
+    assert (host(q) == want_q).all()
+
+
+# ----------------------------------------------------------------- 1-D all-to-all
+
+def run_splits(send, inp):
+    W = send.shape[0]
+    sp = ep.alloc_splits_plan(W)
+    ep.ep_plan_splits(dev(send.astype(np.int64)), sp)
+    out = torch.full((inp.shape[0] * inp.shape[1],) + inp.shape[2:], -1,
+                     dtype=torch.int32 if inp.dtype == np.int32 else torch.int16, device="cuda")
+    ep.ep_dispatch_splits(dev(inp), sp, out)
+    return sp, out
+
+
+def test_splits_worked_example():
+    say("splits worked example")
+    send = np.array([[1, 3], [2, 2]], np.int64)
+    inp = np.zeros((2, 4, 8), np.int32)
+    for i in range(2):
+        for k in range(4):
+            inp[i, k] = 10 * i + k
+    sp, out = run_splits(send, inp)
+    ro = host(sp.rank_offsets)
+    o = host(out)
+    assert o[ro[0]:ro[1], 0].tolist() == [0, 10, 11]
+    assert o[ro[1]:ro[2], 0].tolist() == [1, 2, 3, 12, 13]
+    want = oracle.a2a_plan(send)
+    for f in ("src_offsets", "out_splits", "dst_offsets", "rank_offsets"):
+        assert (host(getattr(sp, f)) == getattr(want, f)).all(), f
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_splits_random(seed):
+    rng = np.random.default_rng(seed)
+    W = int([1, 3, 8, 64][seed])
+    R = int(rng.integers(1, 300))
+    send = np.zeros((W, W), np.int64)
+    for p in range(W):
+        cuts = np.sort(rng.integers(0, R + 1, W - 1))
+        send[p] = np.diff(np.concatenate([[0], cuts, [R]]))
+    send[0, :] = 0
+    send[0, W - 1] = R                       # zero-row chunks
+    inp = rng.integers(0, 1 << 16, size=(W, R, 24)).astype(np.uint16)
+    say("splits random W", W, "R", R)
+    sp, out = run_splits(send, inp)
+    want = oracle.a2a_plan(send)
+    want_out, err = oracle.a2a_copy(inp, want, fill=0xFFFF)
+    assert err == 0
+    assert (host(out, np.uint16) == want_out).all()
+    assert ep.ep_device_error() == 0
+
+
+def test_splits_bad_plan_is_flagged():
+    say("splits bad plan")
+    send = np.array([[1, 3], [2, 2]], np.int64)
+    inp = np.arange(2 * 4 * 8, dtype=np.int32).reshape(2, 4, 8)
+    sp = ep.alloc_splits_plan(2)
+    ep.ep_plan_splits(dev(send), sp)
+    sp.src_offsets[1, 0] = 3                  # would read rows 3..5 of rank 0 (R = 4)
+    out = torch.full((8, 8), -1, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_splits(dev(inp), sp, out)
+    assert ep.ep_device_error() == ep.EP_DEVERR_SPLITS
+    bad = oracle.SplitsPlan(host(sp.src_offsets), host(sp.out_splits), host(sp.dst_offsets),
+                            host(sp.rank_offsets))
+    want, err = oracle.a2a_copy(inp, bad, fill=-1)
+    assert err == oracle.DEVERR_SPLITS
+    assert (host(out) == want).all()
+
+
+def test_splits_config3_full():
+    cfg = workloads.CONFIGS[3]
+    say("splits config 3 full", cfg)
+    send, inp = workloads.splits_inputs(cfg)
+    sp, out = run_splits(send, inp)
+    want = oracle.a2a_plan(send)
+    want_out, err = oracle.a2a_copy(inp, want)
+    assert err == 0
+    assert (host(out, np.uint16) == want_out).all()
