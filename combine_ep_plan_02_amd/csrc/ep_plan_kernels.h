@@ -57,17 +57,18 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tile_kernel(
     int32_t* __restrict__ pos_partial, uint32_t* ticket, uint32_t* flags,
     int32_t* aggregates, int32_t* inclusive) {
   extern __shared__ int32_t lds[];
-  int32_t* hist = lds;                      // [kPlanWaves][E]: counts, then wave-exclusive
-  int32_t* tile_excl = lds + kPlanWaves * E;  // [E]: copies of e in earlier tiles
+  int32_t* hist = lds;                          // [kPlanWaves][E]: counts, then wave-exclusive
+  int32_t* tile_agg = lds + kPlanWaves * E;     // [E]: this tile's counts
+  int32_t* prefix = tile_agg + E;               // [E]: copies of e in earlier tiles
   __shared__ int s_tile;
-  __shared__ uint32_t s_status;
+  __shared__ int s_lo, s_hi, s_incl, s_more;
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
 
   if (tid == 0) s_tile = (int)__hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int i = tid; i < kPlanWaves * E; i += kPlanThreads) hist[i] = 0;
+  for (int i = tid; i < (kPlanWaves + 2) * E; i += kPlanThreads) lds[i] = 0;
   __syncthreads();
   const int b = s_tile;
   if (b >= ntiles) {  // only possible with a workspace that was never initialised
@@ -86,24 +87,34 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tile_kernel(
   const int cs = wave * seg;                       // wave's first copy, tile-relative
   const int ce = min(cs + seg, n);
 
-  // Stable in-wave ranking, chunk by chunk, in flattened (t,k) order.
-  int32_t* myhist = hist + wave * E;
+  // All of the wave's ids (and mask bytes) are requested before any is used.
   int e_reg[kPlanChunks];
-  int r_reg[kPlanChunks];
+  bool act_reg[kPlanChunks];
 #pragma unroll
   for (int ch = 0; ch < kPlanChunks; ++ch) {
     const int c = cs + ch * kWave + lane;
-    const bool valid = c < ce;
-    int e = -1;
-    bool live = false;
-    if (valid) {
+    e_reg[ch] = -1;
+    act_reg[ch] = false;
+    if (c < ce) {
       const int64_t gc = c0 + c;
-      e = ids[gc];
-      const bool act = active == nullptr || active[gc / K] != 0;
-      if (act) {
-        live = (unsigned)e < (unsigned)E;
-        if (!live) raise_device_error(kErrBadExpert);
-      }
+      e_reg[ch] = ids[gc];
+      act_reg[ch] = active == nullptr || active[gc / K] != 0;
+    }
+  }
+
+  // Stable in-wave ranking, chunk by chunk, in flattened (t,k) order: peers
+  // (lanes holding the same expert) come from one ballot per id bit; a lane's
+  // rank is its wave's running count for the expert plus the peers below it;
+  // the highest peer advances the count.
+  int32_t* myhist = hist + wave * E;
+  int r_reg[kPlanChunks];
+#pragma unroll
+  for (int ch = 0; ch < kPlanChunks; ++ch) {
+    const int e = e_reg[ch];
+    bool live = false;
+    if (act_reg[ch]) {
+      live = (unsigned)e < (unsigned)E;
+      if (!live) raise_device_error(kErrBadExpert);
     }
     uint64_t peers = ballot(live);
     for (int bit = 0; bit < id_bits; ++bit) {
@@ -133,61 +144,84 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tile_kernel(
       hist[w * E + e] = run;
       run += v;
     }
-    tile_excl[e] = run;  // the tile's aggregate for now
+    tile_agg[e] = run;
   }
   __syncthreads();
 
   // Decoupled look-back across tiles.
   if (b == 0) {
-    for (int e = tid; e < E; e += kPlanThreads) {
-      inclusive[e] = tile_excl[e];
-      tile_excl[e] = 0;
-    }
+    for (int e = tid; e < E; e += kPlanThreads) inclusive[e] = tile_agg[e];
     __threadfence();
     __syncthreads();
     if (tid == 0)
       __hip_atomic_store(&flags[0], kFlagInclusive, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
   } else {
-    for (int e = tid; e < E; e += kPlanThreads) aggregates[(int64_t)b * E + e] = tile_excl[e];
+    for (int e = tid; e < E; e += kPlanThreads) aggregates[(int64_t)b * E + e] = tile_agg[e];
     __threadfence();
     __syncthreads();
     if (tid == 0)
       __hip_atomic_store(&flags[b], kFlagAggregate, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 
-    // Each thread owns experts tid, tid + 512 (E <= 1024).
-    int ex0 = 0, ex1 = 0;
-    int p = b - 1;
+    // Wave 0 polls a window of up to 64 predecessors at once (lane l: tile
+    // hi - l).  The nearest inclusive prefix in the window ends the walk;
+    // otherwise the whole window's aggregates are added and the window moves
+    // back.  The window's values are summed by all threads in parallel.
+    int hi = b - 1;
     while (true) {
-      if (tid == 0) {
-        uint32_t st = 0;
-        for (int spin = 0; spin < kSpinLimit; ++spin) {
-          st = __hip_atomic_load(&flags[p], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-          if (st != 0) break;
-          __builtin_amdgcn_s_sleep(1);
+      if (wave == 0) {
+        const int p = hi - lane;
+        uint32_t st = kFlagInclusive;  // before tile 0: an empty prefix
+        if (p >= 0) {
+          for (int spin = 0; spin < kSpinLimit; ++spin) {
+            st = __hip_atomic_load(&flags[p], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+            if (st != 0) break;
+            __builtin_amdgcn_s_sleep(1);
+          }
         }
-        if (st == 0) raise_device_error(kErrPlanStall);
-        s_status = st;
+        const uint64_t incl = ballot(p >= 0 && st == kFlagInclusive);
+        const uint64_t none = ballot(p >= 0 && st == 0);
+        if (lane == 0) {
+          if (none) {
+            raise_device_error(kErrPlanStall);
+            s_incl = -1; s_lo = 0; s_hi = -1; s_more = 0;
+          } else if (incl) {
+            const int jn = hi - __builtin_ctzll(incl);   // nearest inclusive prefix
+            s_incl = jn; s_lo = jn + 1; s_hi = hi; s_more = 0;
+          } else {
+            const int lo = hi - (kWave - 1);
+            s_incl = -1; s_lo = lo < 0 ? 0 : lo; s_hi = hi; s_more = lo > 0;
+          }
+        }
       }
       __syncthreads();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-      const uint32_t st = s_status;
-      const int32_t* src = (st == kFlagInclusive) ? inclusive : aggregates;
-      if (st != 0) {
-        if (tid < E) ex0 += src[(int64_t)p * E + tid];
-        if (tid + kPlanThreads < E) ex1 += src[(int64_t)p * E + tid + kPlanThreads];
+      const int lo = s_lo, top = s_hi, jn = s_incl, more = s_more;
+      // Rows lo..top of the aggregates, then row jn of the inclusive prefixes.
+      const int rows = top - lo + 1 + (jn >= 0 ? 1 : 0);
+      const int total = rows * E;
+      for (int base = tid; base < total; base += kPlanThreads * 8) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = base + u * kPlanThreads;
+          v[u] = 0;
+          if (i < total) {
+            const int row = i / E, e = i - row * E;
+            const int q = lo + row;
+            v[u] = q <= top ? aggregates[(int64_t)q * E + e] : inclusive[(int64_t)jn * E + e];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = base + u * kPlanThreads;
+          if (i < total) atomicAdd(&prefix[i % E], v[u]);
+        }
       }
-      __syncthreads();  // s_status is rewritten by the next poll
-      if (st == kFlagInclusive || st == 0 || p == 0) break;
-      --p;
+      __syncthreads();  // the window variables are rewritten by the next poll
+      if (!more) break;
+      hi = lo - 1;
     }
-    if (tid < E) {
-      inclusive[(int64_t)b * E + tid] = ex0 + tile_excl[tid];
-      tile_excl[tid] = ex0;
-    }
-    if (tid + kPlanThreads < E) {
-      inclusive[(int64_t)b * E + tid + kPlanThreads] = ex1 + tile_excl[tid + kPlanThreads];
-      tile_excl[tid + kPlanThreads] = ex1;
-    }
+    for (int e = tid; e < E; e += kPlanThreads) inclusive[(int64_t)b * E + e] = prefix[e] + tile_agg[e];
     __threadfence();
     __syncthreads();
     if (tid == 0)
@@ -201,7 +235,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tile_kernel(
     const int c = cs + ch * kWave + lane;
     if (c < ce) {
       const int e = e_reg[ch];
-      pos_partial[c0 + c] = e >= 0 ? tile_excl[e] + myhist[e] + r_reg[ch] : -1;
+      pos_partial[c0 + c] = e >= 0 ? prefix[e] + myhist[e] + r_reg[ch] : -1;
     }
   }
 }

@@ -15,6 +15,18 @@ namespace ep {
 constexpr int kRowThreads = 256;                       // 4 waves
 constexpr int kTokensPerBlock = kRowThreads / kWave;   // one token per wave
 
+// Cache policy of the row streams: non-temporal (streaming) or default.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+template <bool NT>
+__device__ __forceinline__ void st(u32x4* p, const u32x4 v) {
+  if constexpr (NT) __builtin_nontemporal_store(v, p);
+  else *p = v;
+}
+
 // Lane k < K of a token's wave reads pos[t][k]; a row outside [0, cap_rows)
 // other than -1 is a caller error: it is dropped and flagged, never followed.
 __device__ __forceinline__ int row_of(const int32_t* __restrict__ pos, int t, int K, int lane,
@@ -31,38 +43,42 @@ __device__ __forceinline__ int row_of(const int32_t* __restrict__ pos, int t, in
 // ---------------------------------------------------------------------------
 // Dispatch, bf16 rows: expand_x[pos[t][k]] = x[t] for every live copy
 // (_allToAllV_2d_index_push_kernel on the PyTorch compare view
-// "ciflow/h100-symm-mem/166772" puts one row per (token, k)).  x is read once
-// per token, each row is written K times.
+// "ciflow/h100-symm-mem/166772" puts one row per (token, k)).
+// Work item: one wavefront per (token, column chunk of 64*U vectors), so a
+// launch holds T * ceil(V / 64U) small items and the last wave of items is
+// short (one wave per whole token leaves a long tail at these T).  x is read
+// once per item, each chunk is written to the K rows.
 // ---------------------------------------------------------------------------
-template <int U>
+template <int U, bool NTL, bool NTS>
 __global__ __launch_bounds__(kRowThreads) void dispatch_bf16_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ ex,
-    int T, int K, int V, int64_t cap_rows) {
-  const int t = uniform(blockIdx.x * kTokensPerBlock + (int)(threadIdx.x / kWave));
-  if (t >= T) return;
+    int T, int K, int V, int chunks, int64_t cap_rows) {
+  const int64_t g = (int64_t)blockIdx.x * kTokensPerBlock + uniform((int)(threadIdx.x / kWave));
+  const int64_t t64 = g / chunks;
+  if (t64 >= T) return;
+  const int t = (int)t64;
+  const int v0 = (int)(g - t64 * chunks) * kWave * U;
   const int lane = lane_id();
   const int my_pos = row_of(pos, t, K, lane, cap_rows);
   const uint64_t live = ballot(my_pos >= 0);
   if (live == 0) return;  // inactive token: x is not read
   const u32x4* src = x + (int64_t)t * V;
-  for (int v0 = 0; v0 < V; v0 += kWave * U) {
-    u32x4 r[U];
+  u32x4 r[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) {
+    const int idx = v0 + u * kWave + lane;
+    if (idx < V) r[u] = ld<NTL>(src + idx);
+  }
+  uint64_t m = live;
+  while (m) {
+    const int k = __builtin_ctzll(m);
+    m &= m - 1;
+    const int p = __builtin_amdgcn_readlane(my_pos, k);
+    u32x4* dst = ex + (int64_t)p * V;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int idx = v0 + u * kWave + lane;
-      if (idx < V) r[u] = src[idx];
-    }
-    uint64_t m = live;
-    while (m) {
-      const int k = __builtin_ctzll(m);
-      m &= m - 1;
-      const int p = __builtin_amdgcn_readlane(my_pos, k);
-      u32x4* dst = ex + (int64_t)p * V;
-#pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int idx = v0 + u * kWave + lane;
-        if (idx < V) __builtin_nontemporal_store(r[u], dst + idx);
-      }
+      if (idx < V) st<NTS>(dst + idx, r[u]);
     }
   }
 }
@@ -72,9 +88,6 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_bf16_kernel(
 // of the CANN "aclnnMoeDistributeDispatchV2" page; one fp32 scale per
 // expanded row, as dynamicScalesOut):
 //   scale = fl32(amax / 448),  code = E4M3FN_rne_sat(fl32(x / scale)).
-// The row is read once; the first G groups of 16 values per lane stay in
-// VGPRs between the amax pass and the quantise pass (G*64*16 >= H covers
-// rows up to G*1024 values), longer rows re-read the rest.
 // ---------------------------------------------------------------------------
 
 // fp32 -> E4M3FN, round to nearest even, saturating to +-448; NaN -> 0x7f.
@@ -129,15 +142,21 @@ __device__ __forceinline__ uint32_t amax16_bits(const u32x4 a, const u32x4 b, ui
   return m;
 }
 
-template <int G>
+// One workgroup (4 waves) per token: thread i owns the 16-value groups
+// i, i + 256, ...; the first G of them stay in VGPRs between the amax pass and
+// the quantise pass, longer rows re-read the rest.  The row's amax is
+// reduced across lanes with shuffles and across the 4 waves through LDS.
+template <int G, bool NTL, bool NTS>
 __global__ __launch_bounds__(kRowThreads) void dispatch_fp8_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ q,
     float* __restrict__ scales, int T, int K, int NG, int64_t cap_rows) {
-  const int t = uniform(blockIdx.x * kTokensPerBlock + (int)(threadIdx.x / kWave));
-  if (t >= T) return;
+  __shared__ uint32_t s_max[kRowThreads / kWave];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
   const int lane = lane_id();
+  const int wave = tid / kWave;
   const int my_pos = row_of(pos, t, K, lane, cap_rows);
-  const uint64_t live = ballot(my_pos >= 0);
+  const uint64_t live = ballot(my_pos >= 0);  // the same in every wave of the token
   if (live == 0) return;
   const u32x4* src = x + (int64_t)t * NG * 2;
 
@@ -145,59 +164,69 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_fp8_kernel(
   uint32_t mbits = 0;
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int idx = g * kWave + lane;
+    const int idx = g * kRowThreads + tid;
     if (idx < NG) {
-      cache[g][0] = src[2 * idx];
-      cache[g][1] = src[2 * idx + 1];
+      cache[g][0] = ld<NTL>(src + 2 * idx);
+      cache[g][1] = ld<NTL>(src + 2 * idx + 1);
       mbits = amax16_bits(cache[g][0], cache[g][1], mbits);
     }
   }
-  for (int idx = G * kWave + lane; idx < NG; idx += kWave)
-    mbits = amax16_bits(src[2 * idx], src[2 * idx + 1], mbits);
+  for (int idx = G * kRowThreads + tid; idx < NG; idx += kRowThreads)
+    mbits = amax16_bits(ld<NTL>(src + 2 * idx), ld<NTL>(src + 2 * idx + 1), mbits);
 #pragma unroll
   for (int off = kWave / 2; off > 0; off >>= 1) mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, off, kWave));
-  const float amax = __uint_as_float(uniform((int)mbits) << 16);
+  if (lane == 0) s_max[wave] = mbits;
+  __syncthreads();
+  uint32_t m = s_max[0];
+#pragma unroll
+  for (int w = 1; w < kRowThreads / kWave; ++w) m = max(m, s_max[w]);
+  const float amax = __uint_as_float(m << 16);
   const float scale = amax / 448.0f;
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    const int idx = g * kWave + lane;
+    const int idx = g * kRowThreads + tid;
     if (idx < NG) {
       const u32x4 code = quantize16(cache[g][0], cache[g][1], scale);
-      uint64_t m = live;
-      while (m) {
-        const int k = __builtin_ctzll(m);
-        m &= m - 1;
+      uint64_t mk = live;
+      while (mk) {
+        const int k = __builtin_ctzll(mk);
+        mk &= mk - 1;
         const int p = __builtin_amdgcn_readlane(my_pos, k);
-        __builtin_nontemporal_store(code, q + (int64_t)p * NG + idx);
+        st<NTS>(q + (int64_t)p * NG + idx, code);
       }
     }
   }
-  for (int idx = G * kWave + lane; idx < NG; idx += kWave) {
-    const u32x4 code = quantize16(src[2 * idx], src[2 * idx + 1], scale);
-    uint64_t m = live;
-    while (m) {
-      const int k = __builtin_ctzll(m);
-      m &= m - 1;
+  for (int idx = G * kRowThreads + tid; idx < NG; idx += kRowThreads) {
+    const u32x4 code = quantize16(ld<NTL>(src + 2 * idx), ld<NTL>(src + 2 * idx + 1), scale);
+    uint64_t mk = live;
+    while (mk) {
+      const int k = __builtin_ctzll(mk);
+      mk &= mk - 1;
       const int p = __builtin_amdgcn_readlane(my_pos, k);
-      __builtin_nontemporal_store(code, q + (int64_t)p * NG + idx);
+      st<NTS>(q + (int64_t)p * NG + idx, code);
     }
   }
-  if (my_pos >= 0) scales[my_pos] = scale;
+  if (wave == 0 && my_pos >= 0) scales[my_pos] = scale;
 }
 
 // ---------------------------------------------------------------------------
 // Weighted combine: out[t] = bf16_rne(sum_k w[t][k] * y[pos[t][k]]), fp32
 // fused multiply-adds in increasing k from +0; copies with pos < 0 add
-// nothing.  All K rows of a column block are loaded before the first FMA so
-// the K gathers are in flight together.
+// nothing.  Work item: one wavefront per (token, column chunk of 64*U
+// vectors); all K row chunks are loaded before the first FMA so the K
+// gathers are in flight together.
 // ---------------------------------------------------------------------------
-template <int KMAX, int U>
+template <int KMAX, int U, bool NTL, bool NTS>
 __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     const u32x4* __restrict__ y, const int32_t* __restrict__ pos,
-    const float* __restrict__ w, u32x4* __restrict__ out, int T, int K, int V, int64_t cap_rows) {
-  const int t = uniform(blockIdx.x * kTokensPerBlock + (int)(threadIdx.x / kWave));
-  if (t >= T) return;
+    const float* __restrict__ w, u32x4* __restrict__ out, int T, int K, int V, int chunks,
+    int64_t cap_rows) {
+  const int64_t g = (int64_t)blockIdx.x * kTokensPerBlock + uniform((int)(threadIdx.x / kWave));
+  const int64_t t64 = g / chunks;
+  if (t64 >= T) return;
+  const int t = (int)t64;
+  const int v0 = (int)(g - t64 * chunks) * kWave * U;
   const int lane = lane_id();
   const int my_pos = row_of(pos, t, K, lane, cap_rows);
   const float my_w = lane < K ? w[(int64_t)t * K + lane] : 0.0f;
@@ -208,51 +237,49 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
     pk[k] = __builtin_amdgcn_readlane(my_pos, k);
     wk[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k));
   }
+  u32x4 r[KMAX][U];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (pk[k] >= 0) {
+      const u32x4* row = y + (int64_t)pk[k] * V;
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int idx = v0 + u * kWave + lane;
+        if (idx < V) r[k][u] = ld<NTL>(row + idx);
+      }
+    }
+  }
+  float acc[U][8];
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (pk[k] >= 0) {
+      const float wt = wk[k];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t v4[4] = {r[k][u].x, r[k][u].y, r[k][u].z, r[k][u].w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          acc[u][2 * i] = __builtin_fmaf(wt, bf16lo(v4[i]), acc[u][2 * i]);
+          acc[u][2 * i + 1] = __builtin_fmaf(wt, bf16hi(v4[i]), acc[u][2 * i + 1]);
+        }
+      }
+    }
+  }
   u32x4* dst = out + (int64_t)t * V;
-  for (int v0 = 0; v0 < V; v0 += kWave * U) {
-    u32x4 r[KMAX][U];
 #pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      if (pk[k] >= 0) {
-        const u32x4* row = y + (int64_t)pk[k] * V;
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const int idx = v0 + u * kWave + lane;
-          if (idx < V) r[k][u] = row[idx];
-        }
-      }
-    }
-    float acc[U][8];
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) acc[u][i] = 0.0f;
-#pragma unroll
-    for (int k = 0; k < KMAX; ++k) {
-      if (pk[k] >= 0) {
-        const float wt = wk[k];
-#pragma unroll
-        for (int u = 0; u < U; ++u) {
-          const uint32_t v4[4] = {r[k][u].x, r[k][u].y, r[k][u].z, r[k][u].w};
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            acc[u][2 * i] = __builtin_fmaf(wt, bf16lo(v4[i]), acc[u][2 * i]);
-            acc[u][2 * i + 1] = __builtin_fmaf(wt, bf16hi(v4[i]), acc[u][2 * i + 1]);
-          }
-        }
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int idx = v0 + u * kWave + lane;
-      if (idx < V) {
-        u32x4 o;
-        o.x = f32_to_bf16_rne(acc[u][0]) | (f32_to_bf16_rne(acc[u][1]) << 16);
-        o.y = f32_to_bf16_rne(acc[u][2]) | (f32_to_bf16_rne(acc[u][3]) << 16);
-        o.z = f32_to_bf16_rne(acc[u][4]) | (f32_to_bf16_rne(acc[u][5]) << 16);
-        o.w = f32_to_bf16_rne(acc[u][6]) | (f32_to_bf16_rne(acc[u][7]) << 16);
-        __builtin_nontemporal_store(o, dst + idx);
-      }
+  for (int u = 0; u < U; ++u) {
+    const int idx = v0 + u * kWave + lane;
+    if (idx < V) {
+      u32x4 o;
+      o.x = f32_to_bf16_rne(acc[u][0]) | (f32_to_bf16_rne(acc[u][1]) << 16);
+      o.y = f32_to_bf16_rne(acc[u][2]) | (f32_to_bf16_rne(acc[u][3]) << 16);
+      o.z = f32_to_bf16_rne(acc[u][4]) | (f32_to_bf16_rne(acc[u][5]) << 16);
+      o.w = f32_to_bf16_rne(acc[u][6]) | (f32_to_bf16_rne(acc[u][7]) << 16);
+      st<NTS>(dst + idx, o);
     }
   }
 }
@@ -295,7 +322,7 @@ __global__ __launch_bounds__(kSplitsPlanThreads) void plan_splits_kernel(
 
 // Grid: x = chunk q = r * W + p (receiver r, sender p), y = blocks per chunk.
 // Each wave copies whole rows of its chunk, 16-byte vectors, U per lane.
-template <int U>
+template <int U, bool NTL, bool NTS>
 __global__ __launch_bounds__(kRowThreads) void copy_splits_kernel(
     const u32x4* __restrict__ in, u32x4* __restrict__ out, const int64_t* __restrict__ src_offsets,
     const int64_t* __restrict__ out_splits, const int64_t* __restrict__ dst_offsets,
@@ -320,12 +347,12 @@ __global__ __launch_bounds__(kRowThreads) void copy_splits_kernel(
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t idx = v0 + u * kWave + lane;
-        if (idx < Vr) t[u] = s[idx];
+        if (idx < Vr) t[u] = ld<NTL>(s + idx);
       }
 #pragma unroll
       for (int u = 0; u < U; ++u) {
         const int64_t idx = v0 + u * kWave + lane;
-        if (idx < Vr) __builtin_nontemporal_store(t[u], d + idx);
+        if (idx < Vr) st<NTS>(d + idx, t[u]);
       }
     }
   }
