@@ -260,19 +260,24 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
-    # Per-launch durations: HIP events on the launch stream around each call.
+    # Per-launch durations: each phase launched `steps` times back to back
+    # between two HIP events recorded on the launch stream; the average is
+    # the launch duration (one event pair per batch keeps the events' own
+    # cost out of the figure).
     log("[bench] per-phase timing")
-    ev = {name: [] for name, _ in phases}
-    for _ in range(args.steps):
-        for name, fn in phases:
-            a = torch.cuda.Event(enable_timing=True)
-            b = torch.cuda.Event(enable_timing=True)
-            a.record(stream)
+    phase_ms = {}
+    for name, fn in phases:
+        fn()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        for _ in range(args.steps):
             fn()
-            b.record(stream)
-            ev[name].append((a, b))
+        b.record(stream)
+        torch.cuda.synchronize()
+        phase_ms[name] = a.elapsed_time(b) / args.steps
+    step()  # leave the buffers in the state of one whole step
     torch.cuda.synchronize()
-    phase_ms = {n: float(np.mean([a.elapsed_time(b) for a, b in v])) for n, v in ev.items()}
     assert ep.ep_device_error() == 0
 
     N = bench.n_rows()

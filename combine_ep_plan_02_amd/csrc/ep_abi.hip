@@ -10,10 +10,13 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <mutex>
 #include <string>
+#include <unordered_map>
 
 #include "ep_common.h"
 #include "ep_plan_kernels.h"
@@ -102,9 +105,11 @@ PlanGeometry plan_geometry(int32_t T, int32_t K, int32_t W) {
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
 // Workspace: [ticket (256 B)] [flags: ntiles u32] [aggregates: ntiles x E i32]
-//            [inclusive: ntiles x E i32], each region 256-byte aligned.
+//            [inclusive: ntiles x E i32] [descriptors: ntiles x E u64], each
+// region 256-byte aligned.  The look-back path uses ticket, flags,
+// aggregates and inclusive; the fused path only the descriptors.
 struct WorkspaceLayout {
-  size_t flags, aggregates, inclusive, total;
+  size_t flags, aggregates, inclusive, descriptors, total;
 };
 
 WorkspaceLayout workspace_layout(int ntiles, int E) {
@@ -112,8 +117,43 @@ WorkspaceLayout workspace_layout(int ntiles, int E) {
   l.flags = 256;
   l.aggregates = l.flags + round256((size_t)ntiles * 4);
   l.inclusive = l.aggregates + round256((size_t)ntiles * E * 4);
-  l.total = l.inclusive + round256((size_t)ntiles * E * 4);
+  l.descriptors = l.inclusive + round256((size_t)ntiles * E * 4);
+  l.total = l.descriptors + round256((size_t)ntiles * E * 8);
   return l;
+}
+
+// Tiles of the fused plan kernel that fit on the current device at once
+// (workgroups per CU by occupancy times the CU count).  The fused kernel's
+// tiles wait for each other, so it is only used when its whole grid fits; its
+// waits are bounded, so a grid that cannot become resident (the device held
+// by other work for longer than the bound) ends with EP_DEVERR_PLAN_STALL
+// instead of hanging.
+int fused_capacity(int E) {
+  static std::mutex mu;
+  static std::unordered_map<long long, int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  const long long key = ((long long)dev << 32) | (unsigned)E;
+  std::lock_guard<std::mutex> lock(mu);
+  auto it = cache.find(key);
+  if (it != cache.end()) return it->second;
+  int cus = 0, per_cu = 0;
+  int cap = 0;
+  const size_t lds = (size_t)(ep::kPlanWaves + 5) * E * sizeof(int32_t);
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ep::plan_fused_kernel, ep::kPlanThreads, lds) ==
+          hipSuccess)
+    cap = per_cu * cus;
+  (void)hipGetLastError();
+  cache[key] = cap;
+  return cap;
+}
+
+uint32_t next_epoch() {
+  static std::atomic<uint32_t> counter{0};
+  uint32_t e = ++counter;
+  if (e == 0) e = ++counter;
+  return e;
 }
 
 int id_bits_for(int E) {
@@ -206,6 +246,18 @@ EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t*
   int32_t* aggregates = (int32_t*)(ws + l.aggregates);
   int32_t* inclusive = (int32_t*)(ws + l.inclusive);
 
+  if (g.ntiles > 0 && (int64_t)g.ntiles * E <= ep::kFusedMaxDescriptorsPerTile &&
+      g.ntiles <= fused_capacity(E)) {
+    // Single pass: every tile resident at once, counts exchanged through
+    // self-validating descriptors.
+    const size_t lds = (size_t)(ep::kPlanWaves + 5) * E * sizeof(int32_t);
+    uint64_t* desc = (uint64_t*)(ws + l.descriptors);
+    hipLaunchKernelGGL(ep::plan_fused_kernel, dim3(g.ntiles), dim3(ep::kPlanThreads), lds, s, topk_ids, active,
+                       K, E, W, g.Tw, g.tile_tokens, g.tiles_per_rank, g.ntiles, id_bits_for(E), next_epoch(),
+                       desc, plan->pos, plan->occ, plan->in_splits, plan->src_offsets, plan->out_splits,
+                       plan->dst_offsets, plan->expert_counts, plan->expert_offsets, plan->rank_offsets);
+    return launch_status("ep_plan (fused kernel)");
+  }
   if (g.ntiles > 0) {
     const size_t lds = (size_t)(ep::kPlanWaves + 2) * E * sizeof(int32_t);
     hipLaunchKernelGGL(ep::plan_tile_kernel, dim3(g.ntiles), dim3(ep::kPlanThreads), lds, s, topk_ids,

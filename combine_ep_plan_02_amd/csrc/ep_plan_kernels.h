@@ -356,4 +356,245 @@ __global__ __launch_bounds__(kFinalizeThreads) void plan_finalize_kernel(
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Fused single-pass plan for grids whose tiles all fit on the device at once.  Each tile ranks its copies as in
+// plan_tile_kernel, then publishes its per-expert counts as 64-bit
+// descriptors (call epoch << 32 | count) with relaxed device-scope atomic
+// stores: a descriptor carries its own validity, so no cache write-back or
+// invalidate is needed between publishing and reading.  Every tile then reads
+// all tiles' descriptors (polling each until it carries this call's epoch)
+// and derives, per expert, the copies in earlier tiles, the totals, and the
+// copies before its source rank; the final positions and occurrences follow
+// directly from the ranks still held in registers.  Workgroup s < W also
+// writes rank s's rows of the W x E plan arrays.
+// ---------------------------------------------------------------------------
+constexpr int kFusedMaxDescriptorsPerTile = 1 << 16;  // ntiles * E read by every tile
+
+__device__ __forceinline__ uint64_t wait_descriptor(const uint64_t* d, uint32_t epoch) {
+  uint64_t v = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int spin = 0; (uint32_t)(v >> 32) != epoch && spin < kSpinLimit; ++spin) {
+    __builtin_amdgcn_s_sleep(1);
+    v = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  if ((uint32_t)(v >> 32) != epoch) {
+    raise_device_error(kErrPlanStall);
+    return 0;
+  }
+  return v & 0xffffffffull;
+}
+
+// Block-wide exclusive scan of n <= 1024 ints in LDS `a` (in place) for a
+// 512-thread block, 2 consecutive values per thread; returns the total.
+__device__ int block_exclusive_scan_512(int32_t* a, int n, int32_t* wave_sums) {
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int i0 = tid * 2;
+  const int v0 = i0 < n ? a[i0] : 0;
+  const int v1 = i0 + 1 < n ? a[i0 + 1] : 0;
+  const int local = v0 + v1;
+  int incl = local;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off, kWave);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) wave_sums[wave] = incl;
+  __syncthreads();
+  int base = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kPlanWaves; ++w) {
+    const int ws = wave_sums[w];
+    if (w < wave) base += ws;
+    total += ws;
+  }
+  const int ex = base + incl - local;
+  if (i0 < n) a[i0] = ex;
+  if (i0 + 1 < n) a[i0 + 1] = ex + v0;
+  __syncthreads();
+  return total;
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ active, int K, int E, int W,
+    int Tw, int tile_tokens, int tiles_per_rank, int ntiles, int id_bits, uint32_t epoch,
+    uint64_t* desc, int32_t* __restrict__ pos, int32_t* __restrict__ occ,
+    int64_t* __restrict__ in_splits, int64_t* __restrict__ src_offsets,
+    int64_t* __restrict__ out_splits, int64_t* __restrict__ dst_offsets,
+    int64_t* __restrict__ expert_counts, int64_t* __restrict__ expert_offsets,
+    int64_t* __restrict__ rank_offsets) {
+  extern __shared__ int32_t lds[];
+  int32_t* hist = lds;                       // [kPlanWaves][E]
+  int32_t* tot = hist + kPlanWaves * E;      // [E] all tiles -> expert offsets
+  int32_t* pre = tot + E;                    // [E] tiles before this one
+  int32_t* rbase = pre + E;                  // [E] tiles before this tile's rank
+  int32_t* rin = rbase + E;                  // [E] tiles of rank blockIdx.x (if < W)
+  int32_t* rbg = rin + E;                    // [E] tiles before rank blockIdx.x
+  __shared__ int32_t wave_sums[kPlanWaves];
+
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int b = blockIdx.x;
+  for (int i = tid; i < (kPlanWaves + 5) * E; i += kPlanThreads) lds[i] = 0;
+
+  const int s = b / tiles_per_rank;
+  const int j = b - s * tiles_per_rank;
+  const int64_t t0 = (int64_t)s * Tw + (int64_t)j * tile_tokens;
+  int64_t t1 = t0 + tile_tokens;
+  if (t1 > (int64_t)(s + 1) * Tw) t1 = (int64_t)(s + 1) * Tw;
+  const int64_t c0 = t0 * K;
+  const int n = (int)((t1 - t0) * K);
+  const int seg = (n + kPlanWaves - 1) / kPlanWaves;
+  const int cs = wave * seg;
+  const int ce = min(cs + seg, n);
+
+  int e_reg[kPlanChunks];
+  bool act_reg[kPlanChunks];
+#pragma unroll
+  for (int ch = 0; ch < kPlanChunks; ++ch) {
+    const int c = cs + ch * kWave + lane;
+    e_reg[ch] = -1;
+    act_reg[ch] = false;
+    if (c < ce) {
+      const int64_t gc = c0 + c;
+      e_reg[ch] = ids[gc];
+      act_reg[ch] = active == nullptr || active[gc / K] != 0;
+    }
+  }
+  __syncthreads();  // LDS zeroed
+
+  int32_t* myhist = hist + wave * E;
+  int r_reg[kPlanChunks];
+#pragma unroll
+  for (int ch = 0; ch < kPlanChunks; ++ch) {
+    const int e = e_reg[ch];
+    bool live = false;
+    if (act_reg[ch]) {
+      live = (unsigned)e < (unsigned)E;
+      if (!live) raise_device_error(kErrBadExpert);
+    }
+    uint64_t peers = ballot(live);
+    for (int bit = 0; bit < id_bits; ++bit) {
+      const bool set = (e >> bit) & 1;
+      const uint64_t ones = ballot(live && set);
+      peers &= set ? ones : ~ones;
+    }
+    int r = 0;
+    if (live) {
+      const int below = __popcll(peers & lanemask_lt());
+      const int base = myhist[e];
+      r = base + below;
+      if ((peers >> lane) == 1ull) myhist[e] = base + __popcll(peers);
+    }
+    e_reg[ch] = live ? e : -1;
+    r_reg[ch] = r;
+    __builtin_amdgcn_wave_barrier();
+  }
+  __syncthreads();
+
+  // Wave-exclusive prefixes and this tile's counts, published at once.
+  for (int e = tid; e < E; e += kPlanThreads) {
+    int run = 0;
+#pragma unroll
+    for (int w = 0; w < kPlanWaves; ++w) {
+      const int v = hist[w * E + e];
+      hist[w * E + e] = run;
+      run += v;
+    }
+    __hip_atomic_store(&desc[(int64_t)b * E + e], ((uint64_t)epoch << 32) | (uint32_t)run,
+                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
+  // Read every tile's counts.  Thread (e, h) sums tiles p = h, h + tpe, ...
+  // for expert e in registers (tpe threads per expert), E > 512 gives a
+  // thread two experts.
+  const int g = b;  // this workgroup also writes rank g's plan rows when g < W
+  const int first_s = s * tiles_per_rank;
+  const int first_g = g * tiles_per_rank, last_g = first_g + tiles_per_rank - 1;
+  const int tpe = E >= kPlanThreads ? 1 : kPlanThreads / E;
+  const int n_exp = E > kPlanThreads ? 2 : 1;
+  if (tid < tpe * E || E > kPlanThreads) {
+    for (int xe = 0; xe < n_exp; ++xe) {
+      const int e = E > kPlanThreads ? tid + xe * kPlanThreads : tid % E;
+      const int h = E >= kPlanThreads ? 0 : tid / E;
+      if (e >= E) continue;
+      int a_tot = 0, a_pre = 0, a_rbase = 0, a_rin = 0, a_rbg = 0;
+      for (int p0 = h; p0 < ntiles; p0 += tpe * 8) {
+        uint64_t raw[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int p = p0 + u * tpe;
+          raw[u] = p < ntiles ? __hip_atomic_load(&desc[(int64_t)p * E + e], __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                              : ((uint64_t)epoch << 32);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int p = p0 + u * tpe;
+          if (p >= ntiles) continue;
+          int v = (uint32_t)(raw[u] >> 32) == epoch ? (int)(raw[u] & 0xffffffffull)
+                                                     : (int)wait_descriptor(&desc[(int64_t)p * E + e], epoch);
+          a_tot += v;
+          if (p < b) a_pre += v;
+          if (p < first_s) a_rbase += v;
+          if (p >= first_g && p <= last_g) a_rin += v;
+          if (p < first_g) a_rbg += v;
+        }
+      }
+      if (tpe == 1) {
+        tot[e] = a_tot; pre[e] = a_pre; rbase[e] = a_rbase; rin[e] = a_rin; rbg[e] = a_rbg;
+      } else {
+        atomicAdd(&tot[e], a_tot);
+        atomicAdd(&pre[e], a_pre);
+        atomicAdd(&rbase[e], a_rbase);
+        atomicAdd(&rin[e], a_rin);
+        atomicAdd(&rbg[e], a_rbg);
+      }
+    }
+  }
+  __syncthreads();
+
+  // Final positions and occurrences of this tile's copies.
+  int32_t* eoff = tot;  // scanned in place below; totals copied out first
+  if (g == 0)
+    for (int e = tid; e < E; e += kPlanThreads) expert_counts[e] = tot[e];
+  __syncthreads();
+  const int n_live = block_exclusive_scan_512(eoff, E, wave_sums);
+#pragma unroll
+  for (int ch = 0; ch < kPlanChunks; ++ch) {
+    const int c = cs + ch * kWave + lane;
+    if (c < ce) {
+      const int e = e_reg[ch];
+      int p = -1, o = -1;
+      if (e >= 0) {
+        const int within = pre[e] + myhist[e] + r_reg[ch];  // earlier copies of e, all tiles
+        p = eoff[e] + within;
+        o = within - rbase[e];
+      }
+      pos[c0 + c] = p;
+      if (occ) occ[c0 + c] = o;
+    }
+  }
+
+  if (g == 0) {
+    for (int e = tid; e < E; e += kPlanThreads) expert_offsets[e] = eoff[e];
+    const int ne = E / W;
+    for (int d = tid; d <= W; d += kPlanThreads) rank_offsets[d] = d < W ? eoff[d * ne] : n_live;
+  }
+  if (g < W) {
+    const int ne = E / W;
+    for (int e = tid; e < E; e += kPlanThreads) {
+      const int cnt = rin[e];
+      in_splits[(int64_t)g * E + e] = cnt;
+      out_splits[(int64_t)e * W + g] = cnt;
+      dst_offsets[(int64_t)g * E + e] = rbg[e] + eoff[e] - eoff[(e / ne) * ne];
+    }
+    __syncthreads();
+    block_exclusive_scan_512(rin, E, wave_sums);
+    for (int e = tid; e < E; e += kPlanThreads) src_offsets[(int64_t)g * E + e] = rin[e];
+  }
+}
+
 }  // namespace ep

@@ -53,7 +53,9 @@ PLAN_CASES = [
     (6144, 3, 48, 48, 0.1, 5, "dup"),       # one expert per rank, 48 ranks
     (512, 4, 4, 2, 0.0, 6, "dup"),          # heavy duplicates in a wave
     (8, 3, 6, 2, 0.0, 7, "dup"),            # tile smaller than a wave
-    (20000, 7, 14, 2, 0.2, 8, "dup"),       # 2 ranks x 35 tiles, long look-back
+    (20000, 7, 14, 2, 0.2, 8, "dup"),       # 2 ranks x 35 tiles
+    (8448, 16, 1024, 2, 0.1, 9, "distinct"),  # 66 tiles x 1024 experts: look-back path
+    (131072, 8, 64, 8, 0.0, 10, "dup"),     # 512 tiles: look-back path (windowed)
 ]
 
 
