@@ -30,6 +30,33 @@ if ROOT not in sys.path:
 HBM_PEAK_GBPS = 8000.0   # MI355X HBM3E, AMD's published peak
 METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 GPU"
 
+# HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and
+# WRITE_SIZE (KiB per dispatch; FETCH_SIZE scaled by 2.0 and WRITE_SIZE by
+# 1.0, the factors a plain 1 GiB copy gives), see profiles/.  They describe
+# the kernels built from the sources whose digest is `source_sha256`; any
+# other build reports traffic as null until the counters are taken again.
+TRAFFIC = {
+    "source_sha256": None,
+    "bytes_per_launch": {},   # {workload: {phase: bytes}}
+}
+
+
+def source_digest() -> str:
+    import hashlib
+    d = os.path.join(ROOT, "combine_ep_plan_02_amd", "csrc")
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(d)):
+        if name.endswith((".h", ".hip")):
+            h.update(name.encode())
+            h.update(open(os.path.join(d, name), "rb").read())
+    return h.hexdigest()
+
+
+def measured_traffic(workload: int, phase: str):
+    if TRAFFIC["source_sha256"] != source_digest():
+        return None
+    return TRAFFIC["bytes_per_launch"].get(str(workload), {}).get(phase)
+
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
@@ -44,6 +71,9 @@ def parse():
                     help="index of the workload (2: T=8192 H=7168 E=256 K=8 W=16 Zipf)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain device copy of BYTES bytes 5 times (a known-size "
+                         "reference for the HBM byte counters) and exit")
     return ap.parse_args()
 
 
@@ -232,6 +262,15 @@ def main():
               flush=True)
         sys.exit(2)
     import torch
+    if args.copy_calibration:
+        n = args.copy_calibration
+        src = torch.ones(n, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": n, "launches": 5}), flush=True)
+        return
     import combine_ep_plan_02_amd as ep
     import workloads
 
@@ -299,10 +338,12 @@ def main():
         "hbm_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
         "rows_N": N,
+        "source_sha256": source_digest(),
         "phase_us": {k: v * 1e3 for k, v in phase_ms.items()},
         "phase_gbps": {k: bpp[k] / (phase_ms[k] * 1e-3) / 1e9 for k in phase_ms},
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
-                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS, "traffic": None,
+                     "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
+                     "traffic": measured_traffic(args.workload, dominant),
                      "algorithmic_bytes_per_launch": bpp[dominant]},
     }
     if not args.no_cpu_baseline:

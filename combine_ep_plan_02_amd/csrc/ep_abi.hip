@@ -25,15 +25,18 @@
 #define EP_EXPORT extern "C" __attribute__((visibility("default")))
 
 // Cache policy of each row stream (true: non-temporal), chosen by measurement
-// on MI355X: streaming loads of data read once reach ~7.1 TB/s against ~6.4
-// TB/s for default loads; stores keep the default policy.
+// on MI355X in the dispatch -> combine sequence: streaming stores for every
+// row written (expandX, the combined rows, the all-to-all receive buffer);
+// streaming loads for the combine's gathered rows (~7.1 TB/s for streaming
+// reads against ~6.4 TB/s for default reads); default loads for x and the
+// all-to-all input, which measured faster next to streaming stores.
 constexpr bool kDispatchNtLoad = false, kDispatchNtStore = true;
 constexpr bool kCombineNtLoad = true, kCombineNtStore = true;
 constexpr bool kFp8NtLoad = false, kFp8NtStore = true;
+constexpr bool kCopyNtLoad = false, kCopyNtStore = true;
 // Vectors per lane of one (token, column chunk) work item.
 constexpr int kDispatchUnroll = 2;
 constexpr int kCombineUnroll = 1;
-constexpr bool kCopyNtLoad = true, kCopyNtStore = true;
 
 namespace {
 
