@@ -299,6 +299,25 @@ def main():
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / args.steps
 
+    # Cold steps: before every step the 256 MB Infinity Cache is refilled with
+    # clean lines of an unrelated 512 MB buffer (a read-only reduction, not
+    # timed, after one synchronisation), so no input or output of the
+    # previous step is served from it and no dirty line is left to write back.
+    log("[bench] cold steps")
+    scratch = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    cold = []
+    for _ in range(args.steps):
+        scratch.sum()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        cold.append((a, b))
+    torch.cuda.synchronize()
+    cold_ms = float(np.mean([a.elapsed_time(b) for a, b in cold]))
+    del scratch
+
     # Per-launch durations: each phase launched `steps` times back to back
     # between two HIP events recorded on the launch stream; the average is
     # the launch duration (one event pair per batch keeps the events' own
@@ -335,6 +354,8 @@ def main():
         "dtype": bench.dtype(), "data": "synthetic (seeded numpy generators, see workloads.py)",
         "config": bench.config_record(),
         "hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
+        "cold_ms_per_step": cold_ms,
+        "cold_hbm_gbps": step_bytes / (cold_ms * 1e-3) / 1e9,
         "hbm_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
         "rows_N": N,

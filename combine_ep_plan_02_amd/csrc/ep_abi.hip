@@ -10,7 +10,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
@@ -25,11 +24,13 @@
 #define EP_EXPORT extern "C" __attribute__((visibility("default")))
 
 // Cache policy of each row stream (true: non-temporal), chosen by measurement
-// on MI355X in the dispatch -> combine sequence: streaming stores for every
-// row written (expandX, the combined rows, the all-to-all receive buffer);
-// streaming loads for the combine's gathered rows (~7.1 TB/s for streaming
-// reads against ~6.4 TB/s for default reads); default loads for x and the
-// all-to-all input, which measured faster next to streaming stores.
+// on MI355X in the plan -> dispatch -> combine sequence: streaming stores for
+// every row written (expandX, the combined rows, the all-to-all receive
+// buffer), so no dirty lines are left in the 256 MB Infinity Cache for the
+// next kernel to write back; streaming loads for the combine's gathered rows
+// (~7.1 TB/s for streaming reads against ~6.4 TB/s for default reads);
+// default loads for x and the all-to-all input, which measured faster next
+// to streaming stores.
 constexpr bool kDispatchNtLoad = false, kDispatchNtStore = true;
 constexpr bool kCombineNtLoad = true, kCombineNtStore = true;
 constexpr bool kFp8NtLoad = false, kFp8NtStore = true;
@@ -107,7 +108,7 @@ PlanGeometry plan_geometry(int32_t T, int32_t K, int32_t W) {
 
 size_t round256(size_t n) { return (n + 255) & ~(size_t)255; }
 
-// Workspace: [ticket (256 B)] [flags: ntiles u32] [aggregates: ntiles x E i32]
+// Workspace: [header (256 B): ticket, epoch, done] [flags: ntiles u32] [aggregates: ntiles x E i32]
 //            [inclusive: ntiles x E i32] [descriptors: ntiles x E u64], each
 // region 256-byte aligned.  The look-back path uses ticket, flags,
 // aggregates and inclusive; the fused path only the descriptors.
@@ -150,13 +151,6 @@ int fused_capacity(int E) {
   (void)hipGetLastError();
   cache[key] = cap;
   return cap;
-}
-
-uint32_t next_epoch() {
-  static std::atomic<uint32_t> counter{0};
-  uint32_t e = ++counter;
-  if (e == 0) e = ++counter;
-  return e;
 }
 
 int id_bits_for(int E) {
@@ -244,7 +238,8 @@ EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t*
 
   hipStream_t s = (hipStream_t)stream;
   uint8_t* ws = (uint8_t*)workspace;
-  uint32_t* ticket = (uint32_t*)ws;
+  uint32_t* header = (uint32_t*)ws;
+  uint32_t* ticket = header + ep::kHeaderTicket;
   uint32_t* flags = (uint32_t*)(ws + l.flags);
   int32_t* aggregates = (int32_t*)(ws + l.aggregates);
   int32_t* inclusive = (int32_t*)(ws + l.inclusive);
@@ -256,7 +251,7 @@ EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t*
     const size_t lds = (size_t)(ep::kPlanWaves + 5) * E * sizeof(int32_t);
     uint64_t* desc = (uint64_t*)(ws + l.descriptors);
     hipLaunchKernelGGL(ep::plan_fused_kernel, dim3(g.ntiles), dim3(ep::kPlanThreads), lds, s, topk_ids, active,
-                       K, E, W, g.Tw, g.tile_tokens, g.tiles_per_rank, g.ntiles, id_bits_for(E), next_epoch(),
+                       K, E, W, g.Tw, g.tile_tokens, g.tiles_per_rank, g.ntiles, id_bits_for(E), header,
                        desc, plan->pos, plan->occ, plan->in_splits, plan->src_offsets, plan->out_splits,
                        plan->dst_offsets, plan->expert_counts, plan->expert_offsets, plan->rank_offsets);
     return launch_status("ep_plan (fused kernel)");

@@ -370,6 +370,11 @@ __global__ __launch_bounds__(kFinalizeThreads) void plan_finalize_kernel(
 // writes rank s's rows of the W x E plan arrays.
 // ---------------------------------------------------------------------------
 constexpr int kFusedMaxDescriptorsPerTile = 1 << 16;  // ntiles * E read by every tile
+// Workspace header words (u32): the look-back ticket, the fused kernel's
+// epoch and its count of tiles done reading.
+constexpr int kHeaderTicket = 0;
+constexpr int kHeaderEpoch = 1;
+constexpr int kHeaderDone = 2;
 
 __device__ __forceinline__ uint64_t wait_descriptor(const uint64_t* d, uint32_t epoch) {
   uint64_t v = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -418,7 +423,7 @@ __device__ int block_exclusive_scan_512(int32_t* a, int n, int32_t* wave_sums) {
 
 __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
     const int32_t* __restrict__ ids, const uint8_t* __restrict__ active, int K, int E, int W,
-    int Tw, int tile_tokens, int tiles_per_rank, int ntiles, int id_bits, uint32_t epoch,
+    int Tw, int tile_tokens, int tiles_per_rank, int ntiles, int id_bits, uint32_t* header,
     uint64_t* desc, int32_t* __restrict__ pos, int32_t* __restrict__ occ,
     int64_t* __restrict__ in_splits, int64_t* __restrict__ src_offsets,
     int64_t* __restrict__ out_splits, int64_t* __restrict__ dst_offsets,
@@ -437,6 +442,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
   const int lane = lane_id();
   const int wave = tid / kWave;
   const int b = blockIdx.x;
+  // This launch's descriptor tag: one more than the launches completed on
+  // this workspace (kept in the workspace, so replays of a captured graph
+  // get fresh tags too; 0 never tags a descriptor).
+  const uint32_t epoch =
+      __hip_atomic_load(&header[kHeaderEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
   for (int i = tid; i < (kPlanWaves + 5) * E; i += kPlanThreads) lds[i] = 0;
 
   const int s = b / tiles_per_rank;
@@ -555,6 +565,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
     }
   }
   __syncthreads();
+  // The last tile to finish reading advances the workspace's epoch; every
+  // tile read it at its start, before any tile could finish reading.
+  if (tid == 0) {
+    const uint32_t done =
+        __hip_atomic_fetch_add(&header[kHeaderDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == (uint32_t)ntiles - 1u) {
+      __hip_atomic_store(&header[kHeaderDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&header[kHeaderEpoch], epoch == 0xffffffffu ? 0u : epoch, __ATOMIC_RELAXED,
+                         __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 
   // Final positions and occurrences of this tile's copies.
   int32_t* eoff = tot;  // scanned in place below; totals copied out first
