@@ -68,6 +68,11 @@ def _load():
     lib.oracle_dispatch_fp8.restype = ctypes.c_int
     lib.oracle_combine.argtypes = [i32, i32, i32, P, i64, P, P, P]
     lib.oracle_combine.restype = ctypes.c_int
+    lib.oracle_plan_ex.argtypes = [i32, i32, i32, i32, P, P, P, i32, i32, i32, P, P, P, P, P, P, P,
+                                   P, P, P, P]
+    lib.oracle_plan_ex.restype = ctypes.c_int
+    lib.oracle_dispatch_weights.argtypes = [i32, i32, P, P, P, i64]
+    lib.oracle_dispatch_weights.restype = ctypes.c_int
     lib.oracle_a2a_plan.argtypes = [i32, P, P, P, P, P]
     lib.oracle_a2a_plan.restype = ctypes.c_int
     lib.oracle_a2a_copy.argtypes = [i32, i64, i64, P, P, P, P, P, P, P]
@@ -145,6 +150,47 @@ def plan(ids: np.ndarray, E: int, W: int, active: np.ndarray | None = None) -> P
                              _ptr(out.pos), _ptr(out.occ), ctypes.byref(err))
     _check(rc, "plan")
     out.err = int(err.value)
+    return out
+
+
+def plan_ex(ids: np.ndarray, E: int, W: int, active: np.ndarray | None = None,
+            active_copies: np.ndarray | None = None, major_align: int = 1,
+            pad_empty: bool = False, token_nums_type: int = 1):
+    """Extended plan (per-copy mask, expert padding, expert token numbers).
+    Returns (Plan, expert_token_nums [W][E/W] int64)."""
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    T, K = ids.shape
+    ne = E // W
+    act = None if active is None else np.ascontiguousarray(active, dtype=np.uint8)
+    actc = None if active_copies is None else np.ascontiguousarray(active_copies, dtype=np.uint8)
+    out = Plan(
+        in_splits=np.zeros((W, E), np.int64), src_offsets=np.zeros((W, E), np.int64),
+        out_splits=np.zeros((W, ne, W), np.int64), dst_offsets=np.zeros((W, E), np.int64),
+        expert_counts=np.zeros(E, np.int64), expert_offsets=np.zeros(E, np.int64),
+        rank_offsets=np.zeros(W + 1, np.int64), pos=np.zeros((T, K), np.int32),
+        occ=np.zeros((T, K), np.int32), err=0)
+    etn = np.zeros((W, ne), np.int64)
+    err = ctypes.c_uint32(0)
+    rc = _load().oracle_plan_ex(T, K, E, W, _ptr(ids), _ptr(act), _ptr(actc), int(major_align),
+                                int(bool(pad_empty)), int(token_nums_type), _ptr(out.in_splits),
+                                _ptr(out.src_offsets), _ptr(out.out_splits), _ptr(out.dst_offsets),
+                                _ptr(out.expert_counts), _ptr(out.expert_offsets),
+                                _ptr(out.rank_offsets), _ptr(out.pos), _ptr(out.occ), _ptr(etn),
+                                ctypes.byref(err))
+    _check(rc, "plan_ex")
+    out.err = int(err.value)
+    return out, etn
+
+
+def dispatch_weights(pos: np.ndarray, weights: np.ndarray, cap_rows: int,
+                     fill: float = 0.0) -> np.ndarray:
+    """expand_weights [cap_rows] float32: the gate weight of each expanded row."""
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    weights = np.ascontiguousarray(weights, dtype=np.float32)
+    T, K = pos.shape
+    out = np.full(cap_rows, fill, np.float32)
+    _check(_load().oracle_dispatch_weights(T, K, _ptr(pos), _ptr(weights), _ptr(out), cap_rows),
+           "dispatch_weights")
     return out
 
 

@@ -280,6 +280,152 @@ int oracle_plan(int32_t T, int32_t K, int32_t E, int32_t W,
     return ORC_OK;
 }
 
+/* Extended plan: the same quantities with the dispatch options a grouped
+ * expert GEMM consumes.
+ *   active_copies[T][K] (NULL: all): per-copy mask (CANN
+ *       xActiveMaskOptional as a (Bs, K) tensor); a copy is live when its
+ *       token is active, its own mask entry is set and 0 <= e < E.
+ *   major_align >= 1: every expert's rows are padded up to a multiple of
+ *       major_align; with pad_empty an expert without rows still gets
+ *       major_align rows ([P1] test_make_a2a_2d_exchange_plan, the padding
+ *       rule kept as comments: align each expert's sum up, keep empty
+ *       experts at one alignment unit, and let the expert's last source
+ *       rank chunk absorb the padding).  in_splits, out_splits and
+ *       expert_counts stay the true counts; expert_offsets, rank_offsets,
+ *       dst_offsets and pos place each expert's rows at its aligned start,
+ *       padding rows after the rows of its last source rank.
+ *   expert_token_nums[W][ne] (NULL: not written): per destination rank,
+ *       the rows each local expert receives (type 1) or their inclusive
+ *       prefix sum over local experts (type 0) (CANN expertTokenNumsOut,
+ *       expertTokenNumsType; "prefix sum" read as inclusive). */
+int oracle_plan_ex(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t *ids,
+                   const uint8_t *active, const uint8_t *active_copies, int32_t major_align,
+                   int32_t pad_empty, int32_t token_nums_type, int64_t *in_splits,
+                   int64_t *src_offsets, int64_t *out_splits, int64_t *dst_offsets,
+                   int64_t *expert_counts, int64_t *expert_offsets, int64_t *rank_offsets,
+                   int32_t *pos, int32_t *occ, int64_t *expert_token_nums, uint32_t *err)
+{
+    if (T < 0 || K < 1 || E < 1 || W < 1 || E % W != 0 || T % W != 0 || major_align < 1)
+        return ORC_ERR_ARGS;
+    const int64_t Tw = T / W;
+    const int32_t ne = E / W;
+    const int64_t n_copies = (int64_t)T * K;
+    uint32_t flags = 0;
+
+    /* Live copies. */
+    uint8_t *live = (uint8_t *)calloc((size_t)(n_copies > 0 ? n_copies : 1), 1);
+    if (!live)
+        return ORC_ERR_ARGS;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t i = t * K + k;
+            if (active && !active[t])
+                continue;
+            if (active_copies && !active_copies[i])
+                continue;
+            if (ids[i] < 0 || ids[i] >= E) {
+                flags |= ORC_DEVERR_BAD_EXPERT;
+                continue;
+            }
+            live[i] = 1;
+        }
+    }
+
+    /* Counts, true and padded. */
+    for (int64_t i = 0; i < (int64_t)W * E; ++i)
+        in_splits[i] = 0;
+    for (int64_t i = 0; i < n_copies; ++i)
+        if (live[i])
+            in_splits[(i / K / Tw) * E + ids[i]] += 1;
+    int64_t total_rows = 0;
+    for (int32_t e = 0; e < E; ++e) {
+        int64_t c = 0;
+        for (int32_t s = 0; s < W; ++s)
+            c += in_splits[(int64_t)s * E + e];
+        expert_counts[e] = c;
+        int64_t padded = (c + major_align - 1) / major_align * major_align;
+        if (pad_empty && padded == 0)
+            padded = major_align;
+        expert_offsets[e] = total_rows;
+        total_rows += padded;
+    }
+    for (int32_t d = 0; d < W; ++d)
+        rank_offsets[d] = expert_offsets[(int64_t)d * ne];
+    rank_offsets[W] = total_rows;
+
+    for (int32_t s = 0; s < W; ++s) {
+        int64_t run = 0;
+        for (int32_t e = 0; e < E; ++e) {
+            src_offsets[(int64_t)s * E + e] = run;
+            run += in_splits[(int64_t)s * E + e];
+        }
+    }
+    for (int32_t d = 0; d < W; ++d)
+        for (int32_t le = 0; le < ne; ++le)
+            for (int32_t s = 0; s < W; ++s)
+                out_splits[((int64_t)d * ne + le) * W + s] =
+                    in_splits[(int64_t)s * E + (int64_t)d * ne + le];
+    for (int32_t s = 0; s < W; ++s) {
+        for (int32_t e = 0; e < E; ++e) {
+            int64_t down = 0;
+            for (int32_t s2 = 0; s2 < s; ++s2)
+                down += in_splits[(int64_t)s2 * E + e];
+            dst_offsets[(int64_t)s * E + e] = expert_offsets[e] - rank_offsets[e / ne] + down;
+        }
+    }
+
+    int64_t *seen = (int64_t *)calloc((size_t)W * (size_t)E, sizeof(int64_t));
+    if (!seen) {
+        free(live);
+        return ORC_ERR_ARGS;
+    }
+    for (int64_t i = 0; i < n_copies; ++i) {
+        pos[i] = -1;
+        if (occ)
+            occ[i] = -1;
+        if (!live[i])
+            continue;
+        int64_t s = i / K / Tw;
+        int32_t e = ids[i];
+        int64_t o = seen[s * E + e]++;
+        if (occ)
+            occ[i] = (int32_t)o;
+        pos[i] = (int32_t)(rank_offsets[e / ne] + dst_offsets[s * E + e] + o);
+    }
+    free(seen);
+    free(live);
+
+    if (expert_token_nums) {
+        for (int32_t d = 0; d < W; ++d) {
+            int64_t run = 0;
+            for (int32_t le = 0; le < ne; ++le) {
+                int64_t c = expert_counts[(int64_t)d * ne + le];
+                run += c;
+                expert_token_nums[(int64_t)d * ne + le] = token_nums_type == 0 ? run : c;
+            }
+        }
+    }
+    if (err)
+        *err |= flags;
+    return ORC_OK;
+}
+
+/* Gate weights carried to the expanded rows (CANN expandScalesOut: the
+ * weight each expert row is combined with): expand_weights[pos[t][k]] =
+ * w[t][k] for every live copy; other entries are not touched. */
+int oracle_dispatch_weights(int32_t T, int32_t K, const int32_t *pos, const float *w,
+                            float *expand_weights, int64_t cap_rows)
+{
+    for (int64_t i = 0; i < (int64_t)T * K; ++i) {
+        if (pos[i] < 0)
+            continue;
+        if (pos[i] >= cap_rows)
+            return ORC_ERR_ARGS;
+        expand_weights[pos[i]] = w[i];
+    }
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ */
 /* Dispatch.                                                           */
 /* ------------------------------------------------------------------ */
