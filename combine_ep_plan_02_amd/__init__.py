@@ -39,15 +39,21 @@ EP_DEVERR_BAD_ROW = 8
 _STATUS_NAMES = {1: "EP_ERR_NULLPTR", 2: "EP_ERR_INVALID", 3: "EP_ERR_UNSUPPORTED",
                  4: "EP_ERR_WORKSPACE", 5: "EP_ERR_HIP"}
 
-EXPORTED = ("ep_supported", "ep_workspace_size", "ep_workspace_init", "ep_plan", "ep_dispatch",
-            "ep_combine", "ep_plan_splits", "ep_dispatch_splits", "ep_last_error",
-            "ep_device_error")
+EXPORTED = ("ep_supported", "ep_workspace_size", "ep_workspace_init", "ep_expand_rows_bound",
+            "ep_plan", "ep_dispatch", "ep_combine", "ep_plan_splits", "ep_dispatch_splits",
+            "ep_last_error", "ep_device_error")
 
 
 class EPError(RuntimeError):
     def __init__(self, status: int, message: str):
         super().__init__(f"{_STATUS_NAMES.get(status, status)}: {message}")
         self.status = status
+
+
+class _PlanOpts(ctypes.Structure):
+    _fields_ = [("active_copies", ctypes.c_void_p), ("major_align", ctypes.c_int32),
+                ("pad_empty_experts", ctypes.c_int32), ("expert_token_nums_type", ctypes.c_int32),
+                ("reserved", ctypes.c_int32), ("expert_token_nums", ctypes.c_void_p)]
 
 
 class _PlanT(ctypes.Structure):
@@ -67,8 +73,10 @@ def _load() -> ctypes.CDLL:
         "ep_supported": ([i32, i32, i32, i32, i32, i32], ctypes.c_int),
         "ep_workspace_size": ([i32, i32, i32, i32], sz),
         "ep_workspace_init": ([P, sz, P], ctypes.c_int),
-        "ep_plan": ([i32, i32, i32, i32, P, P, ctypes.POINTER(_PlanT), P, sz, P], ctypes.c_int),
-        "ep_dispatch": ([i32, i32, i32, P, P, i32, P, P, i64, P], ctypes.c_int),
+        "ep_expand_rows_bound": ([i32, i32, i32, i32, i32], i64),
+        "ep_plan": ([i32, i32, i32, i32, P, P, ctypes.POINTER(_PlanOpts), ctypes.POINTER(_PlanT), P,
+                     sz, P], ctypes.c_int),
+        "ep_dispatch": ([i32, i32, i32, P, P, i32, P, P, P, P, i64, P], ctypes.c_int),
         "ep_combine": ([i32, i32, i32, P, i64, P, P, P, P], ctypes.c_int),
         "ep_plan_splits": ([i32, P, P, P, P, P, P], ctypes.c_int),
         "ep_dispatch_splits": ([i32, i64, i64, P, P, P, P, P, P, P], ctypes.c_int),
@@ -187,12 +195,32 @@ def alloc_plan(T: int, K: int, E: int, W: int, device="cuda", with_occ: bool = T
         occ=torch.empty((T, K), dtype=torch.int32, device=device) if with_occ else None)
 
 
+def ep_expand_rows_bound(T: int, K: int, E: int, major_align: int = 1,
+                         pad_empty_experts: bool = False) -> int:
+    return int(lib.ep_expand_rows_bound(T, K, E, major_align, int(bool(pad_empty_experts))))
+
+
 def ep_plan(topk_ids: torch.Tensor, E: int, W: int, plan: Plan, workspace: torch.Tensor,
-            active: torch.Tensor | None = None, stream=None) -> Plan:
+            active: torch.Tensor | None = None, stream=None, *,
+            active_copies: torch.Tensor | None = None, major_align: int = 1,
+            pad_empty_experts: bool = False, expert_token_nums: torch.Tensor | None = None,
+            expert_token_nums_type: int = 1) -> Plan:
     T, K = topk_ids.shape
     st = plan.as_struct()
+    opts = None
+    if (active_copies is not None or major_align != 1 or pad_empty_experts
+            or expert_token_nums is not None):
+        o = _PlanOpts()
+        p = _ptr(active_copies, (torch.uint8, torch.bool), "active_copies")
+        o.active_copies = None if p is None else p.value
+        o.major_align = int(major_align)
+        o.pad_empty_experts = int(bool(pad_empty_experts))
+        o.expert_token_nums_type = int(expert_token_nums_type)
+        p = _ptr(expert_token_nums, torch.int64, "expert_token_nums")
+        o.expert_token_nums = None if p is None else p.value
+        opts = ctypes.byref(o)
     _check(lib.ep_plan(T, K, E, W, _ptr(topk_ids, torch.int32, "topk_ids"),
-                       _ptr(active, (torch.uint8, torch.bool), "active"), ctypes.byref(st),
+                       _ptr(active, (torch.uint8, torch.bool), "active"), opts, ctypes.byref(st),
                        _ptr(workspace, name="workspace"),
                        workspace.numel() * workspace.element_size(), _stream(stream)))
     return plan
@@ -200,7 +228,8 @@ def ep_plan(topk_ids: torch.Tensor, E: int, W: int, plan: Plan, workspace: torch
 
 def ep_dispatch(x: torch.Tensor, pos: torch.Tensor, expand_x: torch.Tensor,
                 expand_scales: torch.Tensor | None = None, out_dtype: int = EP_BF16,
-                stream=None) -> None:
+                stream=None, *, weights: torch.Tensor | None = None,
+                expand_weights: torch.Tensor | None = None) -> None:
     T, H = x.shape
     K = pos.shape[1]
     if pos.shape[0] != T:
@@ -211,6 +240,8 @@ def ep_dispatch(x: torch.Tensor, pos: torch.Tensor, expand_x: torch.Tensor,
     _check(lib.ep_dispatch(T, K, H, _ptr(x, _BITS16, "x"), _ptr(pos, torch.int32, "pos"), out_dtype,
                            _ptr(expand_x, row_dt, "expand_x"),
                            _ptr(expand_scales, torch.float32, "expand_scales"),
+                           _ptr(weights, torch.float32, "weights"),
+                           _ptr(expand_weights, torch.float32, "expand_weights"),
                            expand_x.shape[0], _stream(stream)))
 
 

@@ -126,6 +126,8 @@ WorkspaceLayout workspace_layout(int ntiles, int E) {
   return l;
 }
 
+size_t fused_lds_bytes(int E) { return (size_t)(ep::kPlanWaves + 6) * E * sizeof(int32_t); }
+
 // Tiles of the fused plan kernel that fit on the current device at once
 // (workgroups per CU by occupancy times the CU count).  The fused kernel's
 // tiles wait for each other, so it is only used when its whole grid fits; its
@@ -143,7 +145,7 @@ int fused_capacity(int E) {
   if (it != cache.end()) return it->second;
   int cus = 0, per_cu = 0;
   int cap = 0;
-  const size_t lds = (size_t)(ep::kPlanWaves + 5) * E * sizeof(int32_t);
+  const size_t lds = fused_lds_bytes(E);
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
       hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, ep::plan_fused_kernel, ep::kPlanThreads, lds) ==
           hipSuccess)
@@ -194,11 +196,27 @@ EP_EXPORT int ep_workspace_init(void* workspace, size_t ws_bytes, void* stream) 
   return launch_status("ep_workspace_init");
 }
 
+EP_EXPORT int64_t ep_expand_rows_bound(int32_t T, int32_t K, int32_t E, int32_t major_align,
+                                       int32_t pad_empty_experts) {
+  if (T < 0 || K < 1 || E < 1 || major_align > EP_MAX_ALIGN) return -1;
+  const int64_t a = major_align < 1 ? 1 : major_align;
+  return (int64_t)T * K + (int64_t)E * (pad_empty_experts ? a : a - 1);
+}
+
 EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t* topk_ids,
-                      const uint8_t* active, const ep_plan_t* plan, void* workspace,
-                      size_t ws_bytes, void* stream) {
+                      const uint8_t* active, const ep_plan_opts_t* opts, const ep_plan_t* plan,
+                      void* workspace, size_t ws_bytes, void* stream) {
   int rc = check_dims(T, K, E, W);
   if (rc) return rc;
+  ep_plan_opts_t o{};
+  if (opts) o = *opts;
+  if (o.major_align < 1) o.major_align = 1;
+  if (o.major_align > EP_MAX_ALIGN)
+    return fail(EP_ERR_UNSUPPORTED, "major_align must be <= %d (got %d)", EP_MAX_ALIGN, o.major_align);
+  if (o.expert_token_nums_type != 0 && o.expert_token_nums_type != 1)
+    return fail(EP_ERR_INVALID, "expert_token_nums_type must be 0 or 1 (got %d)", o.expert_token_nums_type);
+  if (ep_expand_rows_bound(T, K, E, o.major_align, o.pad_empty_experts) >= (int64_t)1 << 31)
+    return fail(EP_ERR_UNSUPPORTED, "T*K plus the expert padding must be < 2^31");
   if (!plan) return fail(EP_ERR_NULLPTR, "plan is NULL");
   if (!plan->in_splits || !plan->src_offsets || !plan->out_splits || !plan->dst_offsets ||
       !plan->expert_counts || !plan->expert_offsets || !plan->rank_offsets)
@@ -220,11 +238,15 @@ EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t*
     if (!aligned(outs64[i], 8)) return fail(EP_ERR_INVALID, "plan int64 outputs must be 8-byte aligned");
   if (!aligned(topk_ids, 4) || !aligned(plan->pos, 4) || !aligned(plan->occ, 4))
     return fail(EP_ERR_INVALID, "topk_ids, pos and occ must be 4-byte aligned");
+  if (!aligned(o.expert_token_nums, 8))
+    return fail(EP_ERR_INVALID, "expert_token_nums must be 8-byte aligned");
   // No output may overlap an input or another output.
   struct Range { const void* p; size_t n; const char* name; };
   const Range ranges[] = {
       {topk_ids, (size_t)ncopies * 4, "topk_ids"}, {active, active ? (size_t)T : 0, "active"},
+      {o.active_copies, o.active_copies ? (size_t)ncopies : 0, "active_copies"},
       {workspace, l.total, "workspace"}, {plan->pos, (size_t)ncopies * 4, "pos"},
+      {o.expert_token_nums, o.expert_token_nums ? (size_t)E * 8 : 0, "expert_token_nums"},
       {plan->occ, plan->occ ? (size_t)ncopies * 4 : 0, "occ"},
       {outs64[0], n64[0] * 8, "in_splits"}, {outs64[1], n64[1] * 8, "src_offsets"},
       {outs64[2], n64[2] * 8, "out_splits"}, {outs64[3], n64[3] * 8, "dst_offsets"},
@@ -232,7 +254,7 @@ EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t*
       {outs64[6], n64[6] * 8, "rank_offsets"}};
   const int nr = sizeof ranges / sizeof ranges[0];
   for (int i = 0; i < nr; ++i)
-    for (int j = (i < 2 ? 2 : i + 1); j < nr; ++j)
+    for (int j = (i < 3 ? 3 : i + 1); j < nr; ++j)
       if (overlap(ranges[i].p, ranges[i].n, ranges[j].p, ranges[j].n))
         return fail(EP_ERR_INVALID, "%s overlaps %s", ranges[i].name, ranges[j].name);
 
@@ -248,18 +270,19 @@ EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t*
       g.ntiles <= fused_capacity(E)) {
     // Single pass: every tile resident at once, counts exchanged through
     // self-validating descriptors.
-    const size_t lds = (size_t)(ep::kPlanWaves + 5) * E * sizeof(int32_t);
+    const size_t lds = fused_lds_bytes(E);
     uint64_t* desc = (uint64_t*)(ws + l.descriptors);
     hipLaunchKernelGGL(ep::plan_fused_kernel, dim3(g.ntiles), dim3(ep::kPlanThreads), lds, s, topk_ids, active,
-                       K, E, W, g.Tw, g.tile_tokens, g.tiles_per_rank, g.ntiles, id_bits_for(E), header,
-                       desc, plan->pos, plan->occ, plan->in_splits, plan->src_offsets, plan->out_splits,
+                       o.active_copies, K, E, W, g.Tw, g.tile_tokens, g.tiles_per_rank, g.ntiles, id_bits_for(E),
+                       o.major_align, o.pad_empty_experts ? 1 : 0, o.expert_token_nums_type,
+                       o.expert_token_nums, header, desc, plan->pos, plan->occ, plan->in_splits, plan->src_offsets, plan->out_splits,
                        plan->dst_offsets, plan->expert_counts, plan->expert_offsets, plan->rank_offsets);
     return launch_status("ep_plan (fused kernel)");
   }
   if (g.ntiles > 0) {
     const size_t lds = (size_t)(ep::kPlanWaves + 2) * E * sizeof(int32_t);
     hipLaunchKernelGGL(ep::plan_tile_kernel, dim3(g.ntiles), dim3(ep::kPlanThreads), lds, s, topk_ids,
-                       active, K, E, g.Tw, g.tile_tokens, g.tiles_per_rank, g.ntiles, id_bits_for(E),
+                       active, o.active_copies, K, E, g.Tw, g.tile_tokens, g.tiles_per_rank, g.ntiles, id_bits_for(E),
                        plan->pos, ticket, flags, aggregates, inclusive);
     rc = launch_status("ep_plan (tile kernel)");
     if (rc) return rc;
@@ -269,15 +292,16 @@ EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t*
   if (blocks < W) blocks = W;
   hipLaunchKernelGGL(ep::plan_finalize_kernel, dim3((unsigned)blocks), dim3(ep::kFinalizeThreads), 0, s,
                      topk_ids, ncopies, K, E, W, g.Tw > 0 ? g.Tw : 1, g.tiles_per_rank, g.ntiles,
-                     aggregates, inclusive, flags, ticket, plan->pos, plan->occ, plan->in_splits,
+                     o.major_align, o.pad_empty_experts ? 1 : 0, o.expert_token_nums_type,
+                     o.expert_token_nums, aggregates, inclusive, flags, ticket, plan->pos, plan->occ, plan->in_splits,
                      plan->src_offsets, plan->out_splits, plan->dst_offsets, plan->expert_counts,
                      plan->expert_offsets, plan->rank_offsets);
   return launch_status("ep_plan (finalize kernel)");
 }
 
 EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, const int32_t* pos,
-                          int32_t out_dtype, void* expand_x, float* expand_scales, int64_t cap_rows,
-                          void* stream) {
+                          int32_t out_dtype, void* expand_x, float* expand_scales, const float* weights,
+                          float* expand_weights, int64_t cap_rows, void* stream) {
   if (T < 0) return fail(EP_ERR_INVALID, "T must be >= 0 (got %d)", T);
   if (K < 1 || K > EP_MAX_K) return fail(EP_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)", EP_MAX_K, K);
   int rc = check_rows(H, out_dtype);
@@ -294,6 +318,10 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
     return fail(EP_ERR_INVALID, "x and expand_x must be 16-byte aligned");
   if (!aligned(pos, 4) || (fp8 && !aligned(expand_scales, 4)))
     return fail(EP_ERR_INVALID, "pos and expand_scales must be 4-byte aligned");
+  if ((weights == nullptr) != (expand_weights == nullptr))
+    return fail(EP_ERR_NULLPTR, "weights and expand_weights go together");
+  if (!aligned(weights, 4) || !aligned(expand_weights, 4))
+    return fail(EP_ERR_INVALID, "weights and expand_weights must be 4-byte aligned");
   const size_t xb = (size_t)T * H * 2, pb = (size_t)T * K * 4;
   const size_t eb = (size_t)cap_rows * H * (fp8 ? 1 : 2);
   const size_t sb = fp8 ? (size_t)cap_rows * 4 : 0;
@@ -302,6 +330,12 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
   if (fp8 && (overlap(expand_scales, sb, x, xb) || overlap(expand_scales, sb, pos, pb) ||
               overlap(expand_scales, sb, expand_x, eb)))
     return fail(EP_ERR_INVALID, "expand_scales overlaps another buffer");
+  const size_t wb = expand_weights ? (size_t)cap_rows * 4 : 0;
+  if (expand_weights &&
+      (overlap(expand_weights, wb, x, xb) || overlap(expand_weights, wb, pos, pb) ||
+       overlap(expand_weights, wb, expand_x, eb) || overlap(expand_weights, wb, weights, pb) ||
+       (fp8 && overlap(expand_weights, wb, expand_scales, sb))))
+    return fail(EP_ERR_INVALID, "expand_weights overlaps another buffer");
 
   hipStream_t s = (hipStream_t)stream;
   const dim3 block(ep::kRowThreads);
@@ -313,7 +347,8 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
       return fail(EP_ERR_UNSUPPORTED, "T * H too large for one launch");
     const dim3 cgrid((unsigned)((items + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock));
     hipLaunchKernelGGL((ep::dispatch_bf16_kernel<kDispatchUnroll, kDispatchNtLoad, kDispatchNtStore>), cgrid,
-                       block, 0, s, (const ep::u32x4*)x, pos, (ep::u32x4*)expand_x, T, K, V, chunks, cap_rows);
+                       block, 0, s, (const ep::u32x4*)x, pos, (ep::u32x4*)expand_x, weights, expand_weights, T, K,
+                       V, chunks, cap_rows);
     return launch_status("ep_dispatch (bf16)");
   }
   const int NG = H / 16;
@@ -323,16 +358,16 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
   const int per_thread = (NG + ep::kRowThreads - 1) / ep::kRowThreads;
   if (per_thread <= 1)
     hipLaunchKernelGGL((ep::dispatch_fp8_kernel<1, kFp8NtLoad, kFp8NtStore>), tgrid, block, 0, s, xv, pos, qv,
-                       expand_scales, T, K, NG, cap_rows);
+                       expand_scales, weights, expand_weights, T, K, NG, cap_rows);
   else if (per_thread <= 2)
     hipLaunchKernelGGL((ep::dispatch_fp8_kernel<2, kFp8NtLoad, kFp8NtStore>), tgrid, block, 0, s, xv, pos, qv,
-                       expand_scales, T, K, NG, cap_rows);
+                       expand_scales, weights, expand_weights, T, K, NG, cap_rows);
   else if (per_thread <= 4)
     hipLaunchKernelGGL((ep::dispatch_fp8_kernel<4, kFp8NtLoad, kFp8NtStore>), tgrid, block, 0, s, xv, pos, qv,
-                       expand_scales, T, K, NG, cap_rows);
+                       expand_scales, weights, expand_weights, T, K, NG, cap_rows);
   else
     hipLaunchKernelGGL((ep::dispatch_fp8_kernel<8, kFp8NtLoad, kFp8NtStore>), tgrid, block, 0, s, xv, pos, qv,
-                       expand_scales, T, K, NG, cap_rows);
+                       expand_scales, weights, expand_weights, T, K, NG, cap_rows);
   return launch_status("ep_dispatch (fp8)");
 }
 

@@ -42,6 +42,28 @@ constexpr int kSpinLimit = 1 << 20;  // bounded polling: the kernel always exits
 constexpr int kFinalizeThreads = 256;
 constexpr int kFinalizeCopiesPerThread = 4;
 
+// Rows an expert with `count` rows occupies in expandX: padded up to a
+// multiple of `align`, and one unit for an empty expert with pad_empty.
+__device__ __forceinline__ int padded_rows(int count, int align, int pad_empty) {
+  int p = (count + align - 1) / align * align;
+  if (pad_empty && p == 0) p = align;
+  return p;
+}
+
+// Rank g's expert token numbers: counts (type 1) or their inclusive prefix
+// over the rank's local experts (type 0).
+__device__ void write_expert_token_nums(const int32_t* cnt, int g, int ne, int type, int64_t* out,
+                                        int nthreads) {
+  for (int le = threadIdx.x; le < ne; le += nthreads) {
+    int64_t v = cnt[g * ne + le];
+    if (type == 0) {
+      v = 0;
+      for (int l2 = 0; l2 <= le; ++l2) v += cnt[g * ne + l2];
+    }
+    out[(int64_t)g * ne + le] = v;
+  }
+}
+
 // Tokens per tile: as many as fit kPlanTileCopies copies, never crossing a
 // source rank boundary.
 inline int plan_tile_tokens(int K, int Tw) {
@@ -52,7 +74,8 @@ inline int plan_tile_tokens(int K, int Tw) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_tile_kernel(
-    const int32_t* __restrict__ ids, const uint8_t* __restrict__ active, int K, int E,
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ active,
+    const uint8_t* __restrict__ active_copies, int K, int E,
     int Tw, int tile_tokens, int tiles_per_rank, int ntiles, int id_bits,
     int32_t* __restrict__ pos_partial, uint32_t* ticket, uint32_t* flags,
     int32_t* aggregates, int32_t* inclusive) {
@@ -98,7 +121,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tile_kernel(
     if (c < ce) {
       const int64_t gc = c0 + c;
       e_reg[ch] = ids[gc];
-      act_reg[ch] = active == nullptr || active[gc / K] != 0;
+      act_reg[ch] = (active == nullptr || active[gc / K] != 0) &&
+                    (active_copies == nullptr || active_copies[gc] != 0);
     }
   }
 
@@ -284,13 +308,15 @@ __device__ int block_exclusive_scan_1024(int32_t* a, int n, int32_t* wave_sums) 
 
 __global__ __launch_bounds__(kFinalizeThreads) void plan_finalize_kernel(
     const int32_t* __restrict__ ids, int64_t n_copies, int K, int E, int W, int Tw,
-    int tiles_per_rank, int ntiles, const int32_t* __restrict__ aggregates,
+    int tiles_per_rank, int ntiles, int major_align, int pad_empty, int token_nums_type,
+    int64_t* __restrict__ expert_token_nums, const int32_t* __restrict__ aggregates,
     const int32_t* __restrict__ inclusive, uint32_t* flags, uint32_t* ticket,
     int32_t* __restrict__ pos, int32_t* __restrict__ occ, int64_t* __restrict__ in_splits,
     int64_t* __restrict__ src_offsets, int64_t* __restrict__ out_splits,
     int64_t* __restrict__ dst_offsets, int64_t* __restrict__ expert_counts,
     int64_t* __restrict__ expert_offsets, int64_t* __restrict__ rank_offsets) {
   __shared__ int32_t eoff[1024];
+  __shared__ int32_t cnt[1024];
   __shared__ int32_t row[1024];
   __shared__ int32_t wave_sums[kFinalizeThreads / kWave];
   const int tid = threadIdx.x;
@@ -298,13 +324,19 @@ __global__ __launch_bounds__(kFinalizeThreads) void plan_finalize_kernel(
   const int ne = E / W;
   const int32_t* totals = ntiles > 0 ? inclusive + (int64_t)(ntiles - 1) * E : nullptr;
 
-  for (int e = tid; e < E; e += kFinalizeThreads) eoff[e] = totals ? totals[e] : 0;
+  for (int e = tid; e < E; e += kFinalizeThreads) {
+    const int c = totals ? totals[e] : 0;
+    cnt[e] = c;
+    eoff[e] = padded_rows(c, major_align, pad_empty);
+  }
   __syncthreads();
   const int n_live = block_exclusive_scan_1024(eoff, E, wave_sums);
 
+  if (g < W && expert_token_nums)
+    write_expert_token_nums(cnt, g, ne, token_nums_type, expert_token_nums, kFinalizeThreads);
   if (g == 0) {
     for (int e = tid; e < E; e += kFinalizeThreads) {
-      expert_counts[e] = totals ? totals[e] : 0;
+      expert_counts[e] = cnt[e];
       expert_offsets[e] = eoff[e];
     }
     for (int d = tid; d <= W; d += kFinalizeThreads)
@@ -370,6 +402,7 @@ __global__ __launch_bounds__(kFinalizeThreads) void plan_finalize_kernel(
 // writes rank s's rows of the W x E plan arrays.
 // ---------------------------------------------------------------------------
 constexpr int kFusedMaxDescriptorsPerTile = 1 << 16;  // ntiles * E read by every tile
+constexpr int kDescBatch = 16;                         // descriptor loads in flight per thread
 // Workspace header words (u32): the look-back ticket, the fused kernel's
 // epoch and its count of tiles done reading.
 constexpr int kHeaderTicket = 0;
@@ -422,8 +455,10 @@ __device__ int block_exclusive_scan_512(int32_t* a, int n, int32_t* wave_sums) {
 }
 
 __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
-    const int32_t* __restrict__ ids, const uint8_t* __restrict__ active, int K, int E, int W,
-    int Tw, int tile_tokens, int tiles_per_rank, int ntiles, int id_bits, uint32_t* header,
+    const int32_t* __restrict__ ids, const uint8_t* __restrict__ active,
+    const uint8_t* __restrict__ active_copies, int K, int E, int W, int Tw, int tile_tokens,
+    int tiles_per_rank, int ntiles, int id_bits, int major_align, int pad_empty,
+    int token_nums_type, int64_t* __restrict__ expert_token_nums, uint32_t* header,
     uint64_t* desc, int32_t* __restrict__ pos, int32_t* __restrict__ occ,
     int64_t* __restrict__ in_splits, int64_t* __restrict__ src_offsets,
     int64_t* __restrict__ out_splits, int64_t* __restrict__ dst_offsets,
@@ -436,6 +471,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
   int32_t* rbase = pre + E;                  // [E] tiles before this tile's rank
   int32_t* rin = rbase + E;                  // [E] tiles of rank blockIdx.x (if < W)
   int32_t* rbg = rin + E;                    // [E] tiles before rank blockIdx.x
+  int32_t* cnt = rbg + E;                    // [E] true totals (tot is padded, then scanned)
   __shared__ int32_t wave_sums[kPlanWaves];
 
   const int tid = threadIdx.x;
@@ -447,7 +483,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
   // get fresh tags too; 0 never tags a descriptor).
   const uint32_t epoch =
       __hip_atomic_load(&header[kHeaderEpoch], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1u;
-  for (int i = tid; i < (kPlanWaves + 5) * E; i += kPlanThreads) lds[i] = 0;
+  for (int i = tid; i < (kPlanWaves + 6) * E; i += kPlanThreads) lds[i] = 0;
 
   const int s = b / tiles_per_rank;
   const int j = b - s * tiles_per_rank;
@@ -470,7 +506,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
     if (c < ce) {
       const int64_t gc = c0 + c;
       e_reg[ch] = ids[gc];
-      act_reg[ch] = active == nullptr || active[gc / K] != 0;
+      act_reg[ch] = (active == nullptr || active[gc / K] != 0) &&
+                    (active_copies == nullptr || active_copies[gc] != 0);
     }
   }
   __syncthreads();  // LDS zeroed
@@ -531,17 +568,17 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
       const int h = E >= kPlanThreads ? 0 : tid / E;
       if (e >= E) continue;
       int a_tot = 0, a_pre = 0, a_rbase = 0, a_rin = 0, a_rbg = 0;
-      for (int p0 = h; p0 < ntiles; p0 += tpe * 8) {
-        uint64_t raw[8];
+      for (int p0 = h; p0 < ntiles; p0 += tpe * kDescBatch) {
+        uint64_t raw[kDescBatch];
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kDescBatch; ++u) {
           const int p = p0 + u * tpe;
           raw[u] = p < ntiles ? __hip_atomic_load(&desc[(int64_t)p * E + e], __ATOMIC_RELAXED,
                                                    __HIP_MEMORY_SCOPE_AGENT)
                               : ((uint64_t)epoch << 32);
         }
 #pragma unroll
-        for (int u = 0; u < 8; ++u) {
+        for (int u = 0; u < kDescBatch; ++u) {
           const int p = p0 + u * tpe;
           if (p >= ntiles) continue;
           int v = (uint32_t)(raw[u] >> 32) == epoch ? (int)(raw[u] & 0xffffffffull)
@@ -578,11 +615,16 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
   }
 
   // Final positions and occurrences of this tile's copies.
-  int32_t* eoff = tot;  // scanned in place below; totals copied out first
-  if (g == 0)
-    for (int e = tid; e < E; e += kPlanThreads) expert_counts[e] = tot[e];
+  int32_t* eoff = tot;  // padded, then scanned in place; true totals kept in cnt
+  for (int e = tid; e < E; e += kPlanThreads) {
+    cnt[e] = tot[e];
+    tot[e] = padded_rows(tot[e], major_align, pad_empty);
+    if (g == 0) expert_counts[e] = cnt[e];
+  }
   __syncthreads();
   const int n_live = block_exclusive_scan_512(eoff, E, wave_sums);
+  if (g < W && expert_token_nums)
+    write_expert_token_nums(cnt, g, E / W, token_nums_type, expert_token_nums, kPlanThreads);
 #pragma unroll
   for (int ch = 0; ch < kPlanChunks; ++ch) {
     const int c = cs + ch * kWave + lane;

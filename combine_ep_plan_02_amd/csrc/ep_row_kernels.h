@@ -52,7 +52,8 @@ __device__ __forceinline__ int row_of(const int32_t* __restrict__ pos, int t, in
 template <int U, bool NTL, bool NTS>
 __global__ __launch_bounds__(kRowThreads) void dispatch_bf16_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ ex,
-    int T, int K, int V, int chunks, int64_t cap_rows) {
+    const float* __restrict__ weights, float* __restrict__ expand_weights, int T, int K, int V,
+    int chunks, int64_t cap_rows) {
   const int64_t g = (int64_t)blockIdx.x * kTokensPerBlock + uniform((int)(threadIdx.x / kWave));
   const int64_t t64 = g / chunks;
   if (t64 >= T) return;
@@ -62,6 +63,8 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_bf16_kernel(
   const int my_pos = row_of(pos, t, K, lane, cap_rows);
   const uint64_t live = ballot(my_pos >= 0);
   if (live == 0) return;  // inactive token: x is not read
+  if (v0 == 0 && expand_weights != nullptr && my_pos >= 0)
+    expand_weights[my_pos] = weights[(int64_t)t * K + lane];
   const u32x4* src = x + (int64_t)t * V;
   u32x4 r[U];
 #pragma unroll
@@ -149,7 +152,8 @@ __device__ __forceinline__ uint32_t amax16_bits(const u32x4 a, const u32x4 b, ui
 template <int G, bool NTL, bool NTS>
 __global__ __launch_bounds__(kRowThreads) void dispatch_fp8_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ q,
-    float* __restrict__ scales, int T, int K, int NG, int64_t cap_rows) {
+    float* __restrict__ scales, const float* __restrict__ weights,
+    float* __restrict__ expand_weights, int T, int K, int NG, int64_t cap_rows) {
   __shared__ uint32_t s_max[kRowThreads / kWave];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
@@ -207,7 +211,10 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_fp8_kernel(
       st<NTS>(q + (int64_t)p * NG + idx, code);
     }
   }
-  if (wave == 0 && my_pos >= 0) scales[my_pos] = scale;
+  if (wave == 0 && my_pos >= 0) {
+    scales[my_pos] = scale;
+    if (expand_weights != nullptr) expand_weights[my_pos] = weights[(int64_t)t * K + lane];
+  }
 }
 
 // ---------------------------------------------------------------------------

@@ -94,6 +94,48 @@ typedef struct {
                                 live; may be NULL                                      */
 } ep_plan_t;
 
+/* Options of ep_plan for consumers that read expandX with a grouped expert
+ * GEMM.  A NULL options pointer, or a zero-initialised struct, means: no
+ * per-copy mask, no padding, no expert token numbers.
+ *   active_copies          [T][K] uint8 or NULL: per-copy mask, the (Bs, K)
+ *                          form of xActiveMaskOptional on the CANN dispatch
+ *                          page.  A copy is live iff its token is active
+ *                          (`active`), its own entry is nonzero and its id is
+ *                          in [0, E); a token whose K entries are all zero
+ *                          takes no part.
+ *   major_align            rows of every expert padded up to a multiple of
+ *                          this (<= 0 is read as 1; at most EP_MAX_ALIGN), the
+ *                          major_align of the 2-D all-to-all on the PyTorch
+ *                          compare view: the padding rows follow the rows of
+ *                          the expert's last source rank and are not written.
+ *   pad_empty_experts      nonzero: an expert without rows still gets
+ *                          major_align rows (the same page's test pads empty
+ *                          experts to one unit).
+ *   expert_token_nums_type 1: rows each local expert receives; 0: their
+ *                          inclusive prefix sum over the rank's local experts
+ *                          (expertTokenNumsType on the CANN page).
+ *   expert_token_nums      [W][E/W] int64 device output or NULL.
+ * With padding, expert_offsets / rank_offsets / dst_offsets / pos place
+ * each expert at its aligned start; in_splits, out_splits and expert_counts
+ * stay the true counts; rank_offsets[W] is the padded row total, at most
+ * ep_expand_rows_bound(). */
+typedef struct {
+    const uint8_t *active_copies;
+    int32_t major_align;
+    int32_t pad_empty_experts;
+    int32_t expert_token_nums_type;
+    int32_t reserved;
+    int64_t *expert_token_nums;
+} ep_plan_opts_t;
+
+#define EP_MAX_ALIGN 4096
+
+/* Rows an expandX buffer needs for these dimensions and padding options:
+ * T*K plus, per expert, the most padding it can get (E*(align-1), or
+ * E*align with pad_empty_experts).  Returns -1 for invalid arguments. */
+int64_t ep_expand_rows_bound(int32_t T, int32_t K, int32_t E, int32_t major_align,
+                             int32_t pad_empty_experts);
+
 /* Returns 1 if ep_plan / ep_dispatch / ep_combine accept these dimensions
  * and this row dtype, else 0.  Never fails, never touches the GPU (the
  * availability predicate of ROCm/aiter PR #6960's
@@ -121,13 +163,15 @@ int ep_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  * grouped by destination rank, then local expert, then source rank, then
  * flattened (t,k) order -- the row an index-push puts copy (t,k) to
  * (_allToAllV_2d_index_push_kernel: dst_offsets[expert] + occurrence).
+ * `opts` (NULL: none) adds a per-copy mask, expert padding and expert token
+ * numbers, see ep_plan_opts_t.
  * The result is deterministic and identical to the serial definition.
  * T == 0 writes the all-zero plan.  The workspace (size from
  * ep_workspace_size, initialised once with ep_workspace_init) must not be
  * used by two calls in flight at the same time. */
 int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t *topk_ids,
-            const uint8_t *active, const ep_plan_t *plan, void *workspace,
-            size_t ws_bytes, void *stream);
+            const uint8_t *active, const ep_plan_opts_t *opts, const ep_plan_t *plan,
+            void *workspace, size_t ws_bytes, void *stream);
 
 /* Dispatch scatter: for every copy with pos[t][k] >= 0,
  *   EP_BF16:       expand_x[pos][:] = x[t][:]  (bit copy, H bf16 = 2H bytes)
@@ -138,11 +182,15 @@ int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t *topk_ids,
  *                  (dynamicScalesOut: one fp32 scale per expanded row).
  * x [T][H] bf16; expand_x [cap_rows][H] (uint16 bf16 or uint8 codes);
  * expand_scales [cap_rows] fp32, required for fp8, ignored for bf16.
- * cap_rows >= T*K (the worst case: every copy live).  Rows no copy names
- * are not written.  x, expand_x 16-byte aligned; T == 0 enqueues nothing. */
+ * weights [T][K] fp32 and expand_weights [cap_rows] fp32, both or neither:
+ * expand_weights[pos[t][k]] = weights[t][k], the gate weight carried to each
+ * expanded row (expandScalesOut on the CANN dispatch page).
+ * cap_rows >= T*K (the worst case: every copy live; with expert padding use
+ * ep_expand_rows_bound).  Rows no copy names are not written.  x, expand_x
+ * 16-byte aligned; T == 0 enqueues nothing. */
 int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t *x, const int32_t *pos,
-                int32_t out_dtype, void *expand_x, float *expand_scales, int64_t cap_rows,
-                void *stream);
+                int32_t out_dtype, void *expand_x, float *expand_scales, const float *weights,
+                float *expand_weights, int64_t cap_rows, void *stream);
 
 /* Weighted combine: for every token t and column h,
  *   out[t][h] = bf16_rne( sum over k = 0..K-1 with pos[t][k] >= 0 of

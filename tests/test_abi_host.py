@@ -82,9 +82,9 @@ def plan_struct(ep, base=A, skip=()):
 
 
 def call_plan(ep, T=64, K=2, E=8, W=2, ids=A, active=None, st=None, ws=A + (1 << 36),
-              ws_bytes=1 << 20):
+              ws_bytes=1 << 20, opts=None):
     st = st if st is not None else plan_struct(ep)
-    rc = ep.lib.ep_plan(T, K, E, W, ids, active, ctypes.byref(st), ws, ws_bytes, None)
+    rc = ep.lib.ep_plan(T, K, E, W, ids, active, opts, ctypes.byref(st), ws, ws_bytes, None)
     return rc, ep.lib.ep_last_error().decode()
 
 
@@ -108,24 +108,55 @@ def test_plan_rejections(ep):
     st = plan_struct(ep)
     st.in_splits = st.src_offsets   # two outputs share memory
     assert call_plan(ep, st=st)[0] == ep.EP_ERR_INVALID
-    assert ep.lib.ep_plan(64, 2, 8, 2, A, None, None, A, 1 << 20, None) == ep.EP_ERR_NULLPTR
+    assert ep.lib.ep_plan(64, 2, 8, 2, A, None, None, None, A, 1 << 20, None) == ep.EP_ERR_NULLPTR
+
+
+def test_plan_option_rejections(ep):
+    o = ep._PlanOpts()
+    o.major_align = 5000                       # above EP_MAX_ALIGN
+    assert call_plan(ep, opts=ctypes.byref(o))[0] == ep.EP_ERR_UNSUPPORTED
+    o = ep._PlanOpts()
+    o.expert_token_nums_type = 2
+    assert call_plan(ep, opts=ctypes.byref(o))[0] == ep.EP_ERR_INVALID
+    o = ep._PlanOpts()
+    o.expert_token_nums = A + 4                # misaligned int64 output
+    assert call_plan(ep, opts=ctypes.byref(o))[0] == ep.EP_ERR_INVALID
+    o = ep._PlanOpts()
+    o.expert_token_nums = A                    # aliases topk_ids
+    assert call_plan(ep, opts=ctypes.byref(o))[0] == ep.EP_ERR_INVALID
+    o = ep._PlanOpts()
+    o.active_copies = A + (1 << 30) + 64       # inside in_splits (an output)
+    assert call_plan(ep, opts=ctypes.byref(o))[0] == ep.EP_ERR_INVALID
+
+
+def test_expand_rows_bound(ep):
+    assert ep.ep_expand_rows_bound(64, 2, 8) == 128
+    assert ep.ep_expand_rows_bound(64, 2, 8, 4) == 128 + 8 * 3
+    assert ep.ep_expand_rows_bound(64, 2, 8, 4, True) == 128 + 8 * 4
+    assert ep.ep_expand_rows_bound(64, 2, 8, 0) == 128
+    assert ep.ep_expand_rows_bound(64, 2, 8, 5000) == -1
 
 
 def test_dispatch_rejections(ep):
     d = ep.lib.ep_dispatch
     X, P, EX, S = A, A + (1 << 34), A + (1 << 35), A + (1 << 36)
-    assert d(64, 2, 128, X, P, ep.EP_BF16, EX, None, 127, None) == ep.EP_ERR_INVALID  # cap < T*K
-    assert d(64, 2, 132, X, P, ep.EP_BF16, EX, None, 128, None) == ep.EP_ERR_UNSUPPORTED
-    assert d(64, 2, 136, X, P, ep.EP_FP8_E4M3FN, EX, S, 128, None) == ep.EP_ERR_UNSUPPORTED
-    assert d(64, 2, 128, X, P, 5, EX, None, 128, None) == ep.EP_ERR_INVALID
-    assert d(64, 2, 128, None, P, ep.EP_BF16, EX, None, 128, None) == ep.EP_ERR_NULLPTR
-    assert d(64, 2, 128, X, P, ep.EP_FP8_E4M3FN, EX, None, 128, None) == ep.EP_ERR_NULLPTR
-    assert d(64, 2, 128, X + 8, P, ep.EP_BF16, EX, None, 128, None) == ep.EP_ERR_INVALID
-    assert d(64, 2, 128, X, P, ep.EP_BF16, X + 256, None, 128, None) == ep.EP_ERR_INVALID  # alias
-    assert d(64, 2, 128, X, P, ep.EP_FP8_E4M3FN, EX, EX + 64, 128, None) == ep.EP_ERR_INVALID
-    assert d(64, 0, 128, X, P, ep.EP_BF16, EX, None, 128, None) == ep.EP_ERR_UNSUPPORTED
+    assert d(64, 2, 128, X, P, ep.EP_BF16, EX, None, None, None, 127, None) == ep.EP_ERR_INVALID  # cap < T*K
+    assert d(64, 2, 132, X, P, ep.EP_BF16, EX, None, None, None, 128, None) == ep.EP_ERR_UNSUPPORTED
+    assert d(64, 2, 136, X, P, ep.EP_FP8_E4M3FN, EX, S, None, None, 128, None) == ep.EP_ERR_UNSUPPORTED
+    assert d(64, 2, 128, X, P, 5, EX, None, None, None, 128, None) == ep.EP_ERR_INVALID
+    assert d(64, 2, 128, None, P, ep.EP_BF16, EX, None, None, None, 128, None) == ep.EP_ERR_NULLPTR
+    assert d(64, 2, 128, X, P, ep.EP_FP8_E4M3FN, EX, None, None, None, 128, None) == ep.EP_ERR_NULLPTR
+    assert d(64, 2, 128, X + 8, P, ep.EP_BF16, EX, None, None, None, 128, None) == ep.EP_ERR_INVALID
+    assert d(64, 2, 128, X, P, ep.EP_BF16, X + 256, None, None, None, 128, None) == ep.EP_ERR_INVALID  # alias
+    assert d(64, 2, 128, X, P, ep.EP_FP8_E4M3FN, EX, EX + 64, None, None, 128, None) == ep.EP_ERR_INVALID
+    assert d(64, 0, 128, X, P, ep.EP_BF16, EX, None, None, None, 128, None) == ep.EP_ERR_UNSUPPORTED
+    WT, EW = A + (1 << 37), A + (1 << 38)
+    assert d(64, 2, 128, X, P, ep.EP_BF16, EX, None, WT, None, 128, None) == ep.EP_ERR_NULLPTR
+    assert d(64, 2, 128, X, P, ep.EP_BF16, EX, None, None, EW, 128, None) == ep.EP_ERR_NULLPTR
+    assert d(64, 2, 128, X, P, ep.EP_BF16, EX, None, WT, EW + 2, 128, None) == ep.EP_ERR_INVALID
+    assert d(64, 2, 128, X, P, ep.EP_BF16, EX, None, WT, EX + 64, 128, None) == ep.EP_ERR_INVALID
     # empty input: OK, nothing enqueued, pointers may be NULL
-    assert d(0, 2, 128, None, None, ep.EP_BF16, None, None, 0, None) == ep.EP_OK
+    assert d(0, 2, 128, None, None, ep.EP_BF16, None, None, None, None, 0, None) == ep.EP_OK
 
 
 def test_combine_rejections(ep):
