@@ -71,6 +71,10 @@ def _load():
     lib.oracle_plan_ex.argtypes = [i32, i32, i32, i32, P, P, P, i32, i32, i32, P, P, P, P, P, P, P,
                                    P, P, P, P]
     lib.oracle_plan_ex.restype = ctypes.c_int
+    lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
+    lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
+    lib.oracle_combine_add_rmsnorm.argtypes = [i32, i32, i32, P, i64, P, P, P, P, ctypes.c_float, P, P]
+    lib.oracle_combine_add_rmsnorm.restype = ctypes.c_int
     lib.oracle_dispatch_weights.argtypes = [i32, i32, P, P, P, i64]
     lib.oracle_dispatch_weights.restype = ctypes.c_int
     lib.oracle_a2a_plan.argtypes = [i32, P, P, P, P, P]
@@ -240,6 +244,28 @@ def combine(y_bits: np.ndarray, pos: np.ndarray, weights: np.ndarray) -> np.ndar
     _check(_load().oracle_combine(T, K, H, _ptr(y_bits), cap, _ptr(pos), _ptr(weights),
                                   _ptr(out)), "combine")
     return out
+
+
+def f64_to_bf16_rne(value: float) -> int:
+    return int(_load().oracle_f64_to_bf16_rne(float(value)))
+
+
+def combine_add_rmsnorm(y_bits, pos, weights, residual_bits, gamma_bits, eps: float):
+    """Combine + residual add + RMSNorm.  Returns (residual_out, norm_out),
+    [T][H] uint16 bf16 patterns each."""
+    y_bits = np.ascontiguousarray(y_bits, dtype=np.uint16)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    weights = np.ascontiguousarray(weights, dtype=np.float32)
+    residual_bits = np.ascontiguousarray(residual_bits, dtype=np.uint16)
+    gamma_bits = np.ascontiguousarray(gamma_bits, dtype=np.uint16)
+    T, K = pos.shape
+    cap, H = y_bits.shape
+    ro = np.zeros((T, H), np.uint16)
+    no = np.zeros((T, H), np.uint16)
+    _check(_load().oracle_combine_add_rmsnorm(T, K, H, _ptr(y_bits), cap, _ptr(pos), _ptr(weights),
+                                              _ptr(residual_bits), _ptr(gamma_bits), float(eps),
+                                              _ptr(ro), _ptr(no)), "combine_add_rmsnorm")
+    return ro, no
 
 
 # ---------------------------------------------------------------- 1-D all-to-all

@@ -530,6 +530,84 @@ int oracle_combine(int32_t T, int32_t K, int32_t H, const uint16_t *y,
     return ORC_OK;
 }
 
+/* Round a double to bf16 to nearest, ties to even, in one step (no
+ * intermediate binary32 rounding). */
+uint16_t oracle_f64_to_bf16_rne(double v)
+{
+    if (isnan(v))
+        return 0x7fc0;
+    if (v == 0.0)
+        return signbit(v) ? 0x8000 : 0x0000;
+    /* Candidates: the bf16 values around v.  Truncating the double to
+     * binary32 toward zero and then to bf16 keeps the lower neighbour;
+     * the upper one is the next bf16 pattern away from zero. */
+    double a = fabs(v);
+    uint16_t sign = signbit(v) ? 0x8000 : 0x0000;
+    if (a >= 0x1.ffp127) /* at or past halfway between the largest bf16 and 2^128 */
+        return (uint16_t)(sign | 0x7f80);
+    float f = (float)a; /* nearest float; fix up to truncation below */
+    if ((double)f > a)
+        f = nextafterf(f, 0.0f);
+    uint32_t u;
+    memcpy(&u, &f, sizeof u);
+    uint16_t lo = (uint16_t)(u >> 16);
+    uint16_t hi = (uint16_t)(lo + 1);
+    double dlo = oracle_bf16_to_f32(lo);
+    double dhi = oracle_bf16_to_f32(hi);
+    uint16_t pick;
+    if (a - dlo < dhi - a)
+        pick = lo;
+    else if (a - dlo > dhi - a)
+        pick = hi;
+    else
+        pick = (lo & 1) ? hi : lo;
+    return (uint16_t)(sign | pick);
+}
+
+/* Combine fused with the residual add and RMSNorm of the MoE layer's tail
+ * ([P5] the MoE-finalize + residual + RMSNorm pattern, without the
+ * all-reduce a single GPU does not need; [P4] names CombineAddRmsNorm):
+ *   c    = bf16_rne(sum_k w[t][k] * y[pos[t][k]])   (the combine above)
+ *   h    = bf16_rne(f32(residual[t]) + f32(c))       (residual_out, prenorm)
+ *   n[h] = bf16_rne(h * gamma / sqrt(mean_h(h^2) + eps))   (norm_out)
+ * The sum, the add and the bf16 roundings follow the unfused sequence
+ * (combine, then add, then norm); the norm statistics and the scaling are
+ * taken in double and rounded once. */
+int oracle_combine_add_rmsnorm(int32_t T, int32_t K, int32_t H, const uint16_t *y,
+                               int64_t cap_rows, const int32_t *pos, const float *w,
+                               const uint16_t *residual, const uint16_t *gamma, float eps,
+                               uint16_t *residual_out, uint16_t *norm_out)
+{
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k)
+            if (pos[t * K + k] >= cap_rows)
+                return ORC_ERR_ARGS;
+        double sumsq = 0.0;
+        for (int32_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int32_t k = 0; k < K; ++k) {
+                int64_t p = pos[t * K + k];
+                if (p < 0)
+                    continue;
+                acc = fmaf(w[t * K + k], oracle_bf16_to_f32(y[p * H + h]), acc);
+            }
+            float c = oracle_bf16_to_f32(oracle_f32_to_bf16_rne(acc));
+            float r = oracle_bf16_to_f32(residual[t * (int64_t)H + h]) + c;
+            uint16_t hb = oracle_f32_to_bf16_rne(r);
+            residual_out[t * (int64_t)H + h] = hb;
+            double hv = oracle_bf16_to_f32(hb);
+            sumsq += hv * hv;
+        }
+        double inv = 1.0 / sqrt(sumsq / H + (double)eps);
+        for (int32_t h = 0; h < H; ++h) {
+            double hv = oracle_bf16_to_f32(residual_out[t * (int64_t)H + h]);
+            double g = oracle_bf16_to_f32(gamma[h]);
+            norm_out[t * (int64_t)H + h] = oracle_f64_to_bf16_rne(hv * inv * g);
+        }
+    }
+    return ORC_OK;
+}
+
 /* ------------------------------------------------------------------ */
 /* 1-D uneven all_to_all_single.                                        */
 /* ------------------------------------------------------------------ */
