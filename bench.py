@@ -69,6 +69,10 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4],
                     help="index of the workload (2: T=8192 H=7168 E=256 K=8 W=16 Zipf)")
+    ap.add_argument("--tail", action="store_true",
+                    help="end the step with the fused combine + residual add + RMSNorm tail "
+                         "(ep_combine_add_rmsnorm) instead of ep_combine; the unfused pair "
+                         "ep_combine + ep_add_rmsnorm is timed beside it")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-reps", type=int, default=5)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -80,8 +84,9 @@ def parse():
 # --------------------------------------------------------------------------- MoE
 
 class MoEBench:
-    def __init__(self, cfg, torch, ep, workloads):
+    def __init__(self, cfg, torch, ep, workloads, tail=False):
         self.cfg, self.torch, self.ep = cfg, torch, ep
+        self.tail = tail
         log(f"[bench] generating inputs for {cfg.name}")
         inp = workloads.moe_inputs(cfg)
         self.inp = inp
@@ -110,6 +115,14 @@ class MoEBench:
             self.y = self.ex          # identity expert: combine reads the dispatched rows
         self.out = t.empty((cfg.T, cfg.H), dtype=t.int16, device=dev)
         self.out_dtype = ep.EP_FP8_E4M3FN if cfg.fp8 else ep.EP_BF16
+        if tail:
+            g = t.Generator(device=dev)
+            g.manual_seed(cfg.seed + 2000)
+            self.residual = t.empty((cfg.T, cfg.H), dtype=t.bfloat16, device=dev).normal_(generator=g)
+            self.residual = self.residual.view(t.int16)
+            self.gamma = (1 + 0.1 * t.randn(cfg.H, generator=g, device=dev)).to(t.bfloat16).view(t.int16)
+            self.res_out = t.empty((cfg.T, cfg.H), dtype=t.int16, device=dev)
+            self.norm_out = t.empty((cfg.T, cfg.H), dtype=t.int16, device=dev)
         # sizes for the byte accounting
         live_tok = cfg.T if inp.active is None else int(inp.active.sum())
         self.live_tokens = live_tok
@@ -123,9 +136,24 @@ class MoEBench:
     def combine_step(self):
         self.ep.ep_combine(self.y, self.plan.pos, self.w, self.out)
 
+    def tail_step(self):
+        self.ep.ep_combine_add_rmsnorm(self.y, self.plan.pos, self.w, self.residual, self.gamma,
+                                       1e-6, self.res_out, self.norm_out)
+
+    def add_rmsnorm_step(self):
+        self.ep.ep_add_rmsnorm(self.out, self.residual, self.gamma, 1e-6, self.res_out,
+                               self.norm_out)
+
     def phases(self):
-        return [("ep_plan", self.plan_step), ("ep_dispatch", self.dispatch_step),
-                ("ep_combine", self.combine_step)]
+        last = ("ep_combine_add_rmsnorm", self.tail_step) if self.tail else \
+            ("ep_combine", self.combine_step)
+        return [("ep_plan", self.plan_step), ("ep_dispatch", self.dispatch_step), last]
+
+    def extra_phases(self):
+        """Kernels timed beside the step: the unfused tail pair."""
+        if not self.tail:
+            return []
+        return [("ep_combine", self.combine_step), ("ep_add_rmsnorm", self.add_rmsnorm_step)]
 
     def n_rows(self):
         return int(self.plan.rank_offsets[-1].item())
@@ -140,14 +168,19 @@ class MoEBench:
         row_out = c.H if c.fp8 else 2 * c.H
         disp_b = self.live_tokens * row_in + N * row_out + tk * 4 + (N * 4 if c.fp8 else 0)
         comb_b = N * 2 * c.H + c.T * 2 * c.H + tk * 4 * 2    # rows in, out rows, pos + weights
-        return {"ep_plan": plan_b, "ep_dispatch": disp_b, "ep_combine": comb_b}
+        # fused tail: rows in, residual in, residual_out + norm_out, gamma, pos + weights
+        tail_b = N * 2 * c.H + 3 * c.T * 2 * c.H + 2 * c.H + tk * 4 * 2
+        addn_b = 4 * c.T * 2 * c.H + 2 * c.H                  # x, residual in; two rows out
+        return {"ep_plan": plan_b, "ep_dispatch": disp_b, "ep_combine": comb_b,
+                "ep_combine_add_rmsnorm": tail_b, "ep_add_rmsnorm": addn_b}
 
     def tokens(self):
         return self.cfg.T
 
     def config_record(self):
         c = self.cfg
-        return {"workload": c.name, "T": c.T, "H": c.H, "E": c.E, "K": c.K, "W": c.W,
+        return {"workload": c.name + ("+add_rmsnorm_tail" if self.tail else ""),
+                "T": c.T, "H": c.H, "E": c.E, "K": c.K, "W": c.W,
                 "routing": c.routing + (f"(s={c.zipf_s}, {c.n_empty} empty experts)"
                                         if c.routing == "zipf" else ""),
                 "sigma": c.sigma, "mask_frac": c.mask_frac,
@@ -217,6 +250,9 @@ class SplitsBench:
         return [("ep_plan_splits", lambda: self.ep.ep_plan_splits(self.send, self.sp)),
                 ("ep_dispatch_splits", lambda: self.ep.ep_dispatch_splits(self.inp, self.sp, self.out))]
 
+    def extra_phases(self):
+        return []
+
     def n_rows(self):
         return self.cfg.W * self.cfg.R
 
@@ -275,7 +311,10 @@ def main():
     import workloads
 
     cfg = workloads.CONFIGS[args.workload]
-    bench = (SplitsBench if args.workload == 3 else MoEBench)(cfg, torch, ep, workloads)
+    if args.workload == 3:
+        bench = SplitsBench(cfg, torch, ep, workloads)
+    else:
+        bench = MoEBench(cfg, torch, ep, workloads, tail=args.tail)
     phases = bench.phases()
     stream = torch.cuda.current_stream()
 
@@ -324,7 +363,7 @@ def main():
     # cost out of the figure).
     log("[bench] per-phase timing")
     phase_ms = {}
-    for name, fn in phases:
+    for name, fn in phases + bench.extra_phases():
         fn()
         a = torch.cuda.Event(enable_timing=True)
         b = torch.cuda.Event(enable_timing=True)
@@ -340,8 +379,9 @@ def main():
 
     N = bench.n_rows()
     bpp = bench.bytes_per_phase(N)
-    step_bytes = sum(bpp.values())
-    dominant = max(phase_ms, key=phase_ms.get)
+    step_names = [n for n, _ in phases]
+    step_bytes = sum(bpp[n] for n in step_names)
+    dominant = max(step_names, key=phase_ms.get)
     ach = bpp[dominant] / (phase_ms[dominant] * 1e-3) / 1e9
     tokens = bench.tokens()
     rec = {
@@ -362,6 +402,7 @@ def main():
         "source_sha256": source_digest(),
         "phase_us": {k: v * 1e3 for k, v in phase_ms.items()},
         "phase_gbps": {k: bpp[k] / (phase_ms[k] * 1e-3) / 1e9 for k in phase_ms},
+        "step_phases": step_names,
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(args.workload, dominant),

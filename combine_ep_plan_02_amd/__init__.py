@@ -40,8 +40,8 @@ _STATUS_NAMES = {1: "EP_ERR_NULLPTR", 2: "EP_ERR_INVALID", 3: "EP_ERR_UNSUPPORTE
                  4: "EP_ERR_WORKSPACE", 5: "EP_ERR_HIP"}
 
 EXPORTED = ("ep_supported", "ep_workspace_size", "ep_workspace_init", "ep_expand_rows_bound",
-            "ep_plan", "ep_dispatch", "ep_combine", "ep_plan_splits", "ep_dispatch_splits",
-            "ep_last_error", "ep_device_error")
+            "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_add_rmsnorm", "ep_add_rmsnorm",
+            "ep_plan_splits", "ep_dispatch_splits", "ep_last_error", "ep_device_error")
 
 
 class EPError(RuntimeError):
@@ -78,6 +78,9 @@ def _load() -> ctypes.CDLL:
                      sz, P], ctypes.c_int),
         "ep_dispatch": ([i32, i32, i32, P, P, i32, P, P, P, P, i64, P], ctypes.c_int),
         "ep_combine": ([i32, i32, i32, P, i64, P, P, P, P], ctypes.c_int),
+        "ep_combine_add_rmsnorm": ([i32, i32, i32, P, i64, P, P, P, P, ctypes.c_float, P, P, P],
+                                   ctypes.c_int),
+        "ep_add_rmsnorm": ([i32, i32, P, P, P, ctypes.c_float, P, P, P], ctypes.c_int),
         "ep_plan_splits": ([i32, P, P, P, P, P, P], ctypes.c_int),
         "ep_dispatch_splits": ([i32, i64, i64, P, P, P, P, P, P, P], ctypes.c_int),
         "ep_last_error": ([], ctypes.c_char_p),
@@ -254,6 +257,37 @@ def ep_combine(y: torch.Tensor, pos: torch.Tensor, weights: torch.Tensor, out: t
     _check(lib.ep_combine(T, K, H, _ptr(y, _BITS16, "y"), cap, _ptr(pos, torch.int32, "pos"),
                           _ptr(weights, torch.float32, "weights"), _ptr(out, _BITS16, "out"),
                           _stream(stream)))
+
+
+def ep_combine_add_rmsnorm(y: torch.Tensor, pos: torch.Tensor, weights: torch.Tensor,
+                           residual: torch.Tensor, gamma: torch.Tensor, eps: float,
+                           residual_out: torch.Tensor, norm_out: torch.Tensor, stream=None) -> None:
+    T, K = pos.shape
+    cap, H = y.shape
+    for n, t in (("residual", residual), ("residual_out", residual_out), ("norm_out", norm_out)):
+        if tuple(t.shape) != (T, H):
+            raise ValueError(f"{n} must be [T][H]")
+    if tuple(gamma.shape) != (H,) or tuple(weights.shape) != (T, K):
+        raise ValueError("gamma must be [H] and weights [T][K]")
+    _check(lib.ep_combine_add_rmsnorm(
+        T, K, H, _ptr(y, _BITS16, "y"), cap, _ptr(pos, torch.int32, "pos"),
+        _ptr(weights, torch.float32, "weights"), _ptr(residual, _BITS16, "residual"),
+        _ptr(gamma, _BITS16, "gamma"), float(eps), _ptr(residual_out, _BITS16, "residual_out"),
+        _ptr(norm_out, _BITS16, "norm_out"), _stream(stream)))
+
+
+def ep_add_rmsnorm(x: torch.Tensor, residual: torch.Tensor, gamma: torch.Tensor, eps: float,
+                   residual_out: torch.Tensor, norm_out: torch.Tensor, stream=None) -> None:
+    T, H = x.shape
+    for n, t in (("residual", residual), ("residual_out", residual_out), ("norm_out", norm_out)):
+        if tuple(t.shape) != (T, H):
+            raise ValueError(f"{n} must be [T][H]")
+    if tuple(gamma.shape) != (H,):
+        raise ValueError("gamma must be [H]")
+    _check(lib.ep_add_rmsnorm(T, H, _ptr(x, _BITS16, "x"), _ptr(residual, _BITS16, "residual"),
+                              _ptr(gamma, _BITS16, "gamma"), float(eps),
+                              _ptr(residual_out, _BITS16, "residual_out"),
+                              _ptr(norm_out, _BITS16, "norm_out"), _stream(stream)))
 
 
 # --------------------------------------------------------------------- 1-D path

@@ -410,6 +410,97 @@ EP_EXPORT int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t* y, int
   return launch_status("ep_combine");
 }
 
+namespace {
+
+constexpr int kTailMaxH = 16384;  // 8 vectors per thread of a 256-thread workgroup
+
+int check_tail(int32_t T, int32_t H, const void* residual, const void* gamma, float eps,
+               const void* residual_out, const void* norm_out) {
+  if (T < 0) return fail(EP_ERR_INVALID, "T must be >= 0 (got %d)", T);
+  if (H < 8 || H % 8 || H > kTailMaxH)
+    return fail(EP_ERR_UNSUPPORTED, "H must be a multiple of 8 in [8, %d] (got %d)", kTailMaxH, H);
+  if (!(eps >= 0.0f) || eps > 3.0e38f) return fail(EP_ERR_INVALID, "eps must be finite and >= 0");
+  if (T == 0) return EP_OK;
+  if (!residual || !gamma || !residual_out || !norm_out)
+    return fail(EP_ERR_NULLPTR, "residual, gamma, residual_out and norm_out are required");
+  if (!aligned(residual, 16) || !aligned(gamma, 16) || !aligned(residual_out, 16) || !aligned(norm_out, 16))
+    return fail(EP_ERR_INVALID, "residual, gamma, residual_out and norm_out must be 16-byte aligned");
+  const size_t rb = (size_t)T * H * 2;
+  if (overlap(residual_out, rb, residual, rb) || overlap(residual_out, rb, gamma, (size_t)H * 2) ||
+      overlap(norm_out, rb, residual, rb) || overlap(norm_out, rb, gamma, (size_t)H * 2) ||
+      overlap(norm_out, rb, residual_out, rb))
+    return fail(EP_ERR_INVALID, "residual_out and norm_out must not overlap each other or an input");
+  return EP_OK;
+}
+
+template <int KMAX>
+void launch_tail(int NV, dim3 grid, hipStream_t s, const ep::u32x4* y, const int32_t* pos, const float* w,
+                 const ep::u32x4* x, const ep::u32x4* res, const ep::u32x4* gamma, float eps, ep::u32x4* ro,
+                 ep::u32x4* no, int T, int K, int V, int64_t cap) {
+  const dim3 block(ep::kRowThreads);
+#define EP_TAIL(NVV)                                                                                      \
+  hipLaunchKernelGGL((ep::combine_add_rmsnorm_kernel<KMAX, NVV, kCombineNtLoad, kCombineNtStore>), grid, \
+                     block, 0, s, y, pos, w, x, res, gamma, eps, ro, no, T, K, V, cap)
+  if (NV <= 1) EP_TAIL(1);
+  else if (NV <= 2) EP_TAIL(2);
+  else if (NV <= 4) EP_TAIL(4);
+  else EP_TAIL(8);
+#undef EP_TAIL
+}
+
+}  // namespace
+
+EP_EXPORT int ep_combine_add_rmsnorm(int32_t T, int32_t K, int32_t H, const uint16_t* y, int64_t cap_rows,
+                                     const int32_t* pos, const float* weights, const uint16_t* residual,
+                                     const uint16_t* gamma, float eps, uint16_t* residual_out,
+                                     uint16_t* norm_out, void* stream) {
+  if (K < 1 || K > EP_MAX_K) return fail(EP_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)", EP_MAX_K, K);
+  int rc = check_tail(T, H, residual, gamma, eps, residual_out, norm_out);
+  if (rc) return rc;
+  if ((int64_t)T * K >= (int64_t)1 << 31) return fail(EP_ERR_UNSUPPORTED, "T*K must be < 2^31");
+  if (cap_rows < 0) return fail(EP_ERR_INVALID, "cap_rows must be >= 0");
+  if (T == 0) return ok();
+  if (!y || !pos || !weights) return fail(EP_ERR_NULLPTR, "y, pos and weights are required");
+  if (!aligned(y, 16)) return fail(EP_ERR_INVALID, "y must be 16-byte aligned");
+  if (!aligned(pos, 4) || !aligned(weights, 4)) return fail(EP_ERR_INVALID, "pos and weights must be 4-byte aligned");
+  const size_t rb = (size_t)T * H * 2, yb = (size_t)cap_rows * H * 2, pb = (size_t)T * K * 4;
+  for (const void* o : {(const void*)residual_out, (const void*)norm_out})
+    if (overlap(o, rb, y, yb) || overlap(o, rb, pos, pb) || overlap(o, rb, weights, pb))
+      return fail(EP_ERR_INVALID, "an output overlaps an input");
+  const int V = H / 8;
+  const int NV = (V + ep::kRowThreads - 1) / ep::kRowThreads;
+  hipStream_t s = (hipStream_t)stream;
+  const dim3 grid((unsigned)T);
+  auto args = [&](auto launch) {
+    launch(NV, grid, s, (const ep::u32x4*)y, pos, weights, (const ep::u32x4*)nullptr,
+           (const ep::u32x4*)residual, (const ep::u32x4*)gamma, eps, (ep::u32x4*)residual_out,
+           (ep::u32x4*)norm_out, T, K, V, cap_rows);
+  };
+  if (K <= 4) args(launch_tail<4>);
+  else if (K <= 8) args(launch_tail<8>);
+  else args(launch_tail<16>);
+  return launch_status("ep_combine_add_rmsnorm");
+}
+
+EP_EXPORT int ep_add_rmsnorm(int32_t T, int32_t H, const uint16_t* x, const uint16_t* residual,
+                             const uint16_t* gamma, float eps, uint16_t* residual_out, uint16_t* norm_out,
+                             void* stream) {
+  int rc = check_tail(T, H, residual, gamma, eps, residual_out, norm_out);
+  if (rc) return rc;
+  if (T == 0) return ok();
+  if (!x) return fail(EP_ERR_NULLPTR, "x is required");
+  if (!aligned(x, 16)) return fail(EP_ERR_INVALID, "x must be 16-byte aligned");
+  const size_t rb = (size_t)T * H * 2;
+  if (overlap(residual_out, rb, x, rb) || overlap(norm_out, rb, x, rb))
+    return fail(EP_ERR_INVALID, "an output overlaps x");
+  const int V = H / 8;
+  const int NV = (V + ep::kRowThreads - 1) / ep::kRowThreads;
+  launch_tail<1>(NV, dim3((unsigned)T), (hipStream_t)stream, nullptr, nullptr, nullptr, (const ep::u32x4*)x,
+                 (const ep::u32x4*)residual, (const ep::u32x4*)gamma, eps, (ep::u32x4*)residual_out,
+                 (ep::u32x4*)norm_out, T, 1, V, 0);
+  return launch_status("ep_add_rmsnorm");
+}
+
 EP_EXPORT int ep_plan_splits(int32_t W, const int64_t* in_splits, int64_t* src_offsets,
                              int64_t* out_splits, int64_t* dst_offsets, int64_t* rank_offsets,
                              void* stream) {

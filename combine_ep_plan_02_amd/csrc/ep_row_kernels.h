@@ -292,6 +292,126 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// Combine fused with the layer tail: residual add and RMSNorm (the
+// MoE-finalize + residual + RMSNorm pattern of flashinfer PR #4358, without
+// the all-reduce; CombineAddRmsNorm on the CANN dispatch page):
+//   c = bf16(sum_k w[t][k] y[pos[t][k]]),  h = bf16(residual[t] + c),
+//   norm = bf16(h * gamma / sqrt(mean(h^2) + eps)).
+// One workgroup per token; thread i owns the 16-byte vectors i, i + 256, ...
+// (NV of them, H <= NV * 2048), whose h values stay in VGPRs between the
+// sum-of-squares pass and the scaling pass.  The combined rows never go
+// to HBM.  With y == nullptr the kernel is the tail alone: c = x[t].
+// ---------------------------------------------------------------------------
+template <int KMAX, int NV, bool NTL, bool NTS>
+__global__ __launch_bounds__(kRowThreads) void combine_add_rmsnorm_kernel(
+    const u32x4* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ w,
+    const u32x4* __restrict__ x, const u32x4* __restrict__ residual, const u32x4* __restrict__ gamma,
+    float eps, u32x4* __restrict__ residual_out, u32x4* __restrict__ norm_out, int T, int K, int V,
+    int64_t cap_rows) {
+  __shared__ float s_sum[kRowThreads / kWave];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  int pk[KMAX];
+  float wk[KMAX];
+  if (y != nullptr) {
+    const int my_pos = row_of(pos, t, K, lane, cap_rows);
+    const float my_w = lane < K ? w[(int64_t)t * K + lane] : 0.0f;
+#pragma unroll
+    for (int k = 0; k < KMAX; ++k) {
+      pk[k] = __builtin_amdgcn_readlane(my_pos, k);
+      wk[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k));
+    }
+  }
+  float hv[NV][8];
+  float sumsq = 0.0f;
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = tid + i * kRowThreads;
+    if (v < V) {
+      float c[8];
+      if (y != nullptr) {
+        u32x4 r[KMAX];
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k)
+          if (pk[k] >= 0) r[k] = ld<NTL>(y + (int64_t)pk[k] * V + v);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = 0.0f;
+#pragma unroll
+        for (int k = 0; k < KMAX; ++k) {
+          if (pk[k] >= 0) {
+            const uint32_t v4[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              c[2 * j] = __builtin_fmaf(wk[k], bf16lo(v4[j]), c[2 * j]);
+              c[2 * j + 1] = __builtin_fmaf(wk[k], bf16hi(v4[j]), c[2 * j + 1]);
+            }
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) c[j] = __uint_as_float(f32_to_bf16_rne(c[j]) << 16);
+      } else {
+        const u32x4 xv = ld<NTL>(x + (int64_t)t * V + v);
+        const uint32_t v4[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          c[2 * j] = bf16lo(v4[j]);
+          c[2 * j + 1] = bf16hi(v4[j]);
+        }
+      }
+      const u32x4 rv = ld<NTL>(residual + (int64_t)t * V + v);
+      const uint32_t r4[4] = {rv.x, rv.y, rv.z, rv.w};
+      uint32_t hb[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        hb[2 * j] = f32_to_bf16_rne(bf16lo(r4[j]) + c[2 * j]);
+        hb[2 * j + 1] = f32_to_bf16_rne(bf16hi(r4[j]) + c[2 * j + 1]);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        hv[i][j] = __uint_as_float(hb[j] << 16);
+        sumsq = __builtin_fmaf(hv[i][j], hv[i][j], sumsq);
+      }
+      u32x4 o;
+      o.x = hb[0] | (hb[1] << 16);
+      o.y = hb[2] | (hb[3] << 16);
+      o.z = hb[4] | (hb[5] << 16);
+      o.w = hb[6] | (hb[7] << 16);
+      st<NTS>(residual_out + (int64_t)t * V + v, o);
+    }
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) sumsq += __shfl_xor(sumsq, off, kWave);
+  if (lane == 0) s_sum[wave] = sumsq;
+  __syncthreads();
+  float total = 0.0f;
+#pragma unroll
+  for (int q = 0; q < kRowThreads / kWave; ++q) total += s_sum[q];
+  const float inv = 1.0f / sqrtf(total / (float)(V * 8) + eps);
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    const int v = tid + i * kRowThreads;
+    if (v < V) {
+      const u32x4 gv = gamma[v];
+      const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w};
+      uint32_t nb[8];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        nb[2 * j] = f32_to_bf16_rne(hv[i][2 * j] * inv * bf16lo(g4[j]));
+        nb[2 * j + 1] = f32_to_bf16_rne(hv[i][2 * j + 1] * inv * bf16hi(g4[j]));
+      }
+      u32x4 o;
+      o.x = nb[0] | (nb[1] << 16);
+      o.y = nb[2] | (nb[3] << 16);
+      o.z = nb[4] | (nb[5] << 16);
+      o.w = nb[6] | (nb[7] << 16);
+      st<NTS>(norm_out + (int64_t)t * V + v, o);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
 // 1-D uneven all_to_all_single (test_make_a2a_exchange_plan / allToAllGet on
 // the PyTorch compare view; aws-neuron/torch-neuronx PR #1035).
 // ---------------------------------------------------------------------------

@@ -205,6 +205,30 @@ int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t *x, const int32_
 int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t *y, int64_t cap_rows,
                const int32_t *pos, const float *weights, uint16_t *out, void *stream);
 
+/* Combine fused with the layer tail (the MoE-finalize + residual + RMSNorm
+ * pattern of flashinfer PR #4358 without its all-reduce; CombineAddRmsNorm
+ * on the CANN dispatch page).  For every token t and column h:
+ *   c = bf16_rne(sum_k w[t][k] * y[pos[t][k]][h])        (as ep_combine)
+ *   residual_out[t][h] = bf16_rne(residual[t][h] + c)    (fp32 add)
+ *   norm_out[t][h] = bf16_rne(residual_out[t][h] * gamma[h]
+ *                             / sqrt(mean_h(residual_out[t][h]^2) + eps))
+ * with the mean's sum of squares accumulated in fp32.  The combined rows
+ * are not written (they never reach HBM).  8 <= H <= 16384, H % 8 == 0,
+ * eps >= 0; residual, gamma [H], residual_out, norm_out bf16 16-byte
+ * aligned; outputs must not overlap inputs or each other.  The result is
+ * bit-identical to ep_combine followed by ep_add_rmsnorm. */
+int ep_combine_add_rmsnorm(int32_t T, int32_t K, int32_t H, const uint16_t *y, int64_t cap_rows,
+                           const int32_t *pos, const float *weights, const uint16_t *residual,
+                           const uint16_t *gamma, float eps, uint16_t *residual_out,
+                           uint16_t *norm_out, void *stream);
+
+/* The layer tail alone: residual_out = bf16_rne(residual + x) and norm_out
+ * as above, for x [T][H] bf16 (the unfused second half of
+ * ep_combine_add_rmsnorm).  Same limits. */
+int ep_add_rmsnorm(int32_t T, int32_t H, const uint16_t *x, const uint16_t *residual,
+                   const uint16_t *gamma, float eps, uint16_t *residual_out, uint16_t *norm_out,
+                   void *stream);
+
 /* 1-D uneven all_to_all_single plan (test_make_a2a_exchange_plan on the
  * PyTorch compare view; the uneven-split lowering of aws-neuron/torch-neuronx
  * PR #1035).  in_splits[p][r] = rows rank p sends to rank r.  Outputs,

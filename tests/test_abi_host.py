@@ -196,3 +196,23 @@ def test_last_error_is_cleared_by_predicates(ep):
     assert "K must be" in before
     ep.ep_supported(64, 2, 8, 2, 128)
     assert ep.lib.ep_last_error().decode() == before  # the predicate never clobbers it
+
+
+def test_tail_rejections(ep):
+    f = ep.lib.ep_combine_add_rmsnorm
+    Y, P, Wt, R, G, RO, NO = (A + i * (1 << 34) for i in range(7))
+    ok = dict(T=64, K=2, H=128)
+    assert f(64, 2, 132, Y, 128, P, Wt, R, G, 1e-6, RO, NO, None) == ep.EP_ERR_UNSUPPORTED  # H % 8
+    assert f(64, 2, 16392, Y, 128, P, Wt, R, G, 1e-6, RO, NO, None) == ep.EP_ERR_UNSUPPORTED  # H > 16384
+    assert f(64, 2, 128, Y, 128, P, Wt, R, G, -1.0, RO, NO, None) == ep.EP_ERR_INVALID  # eps < 0
+    assert f(64, 2, 128, Y, 128, P, Wt, R, G, float("nan"), RO, NO, None) == ep.EP_ERR_INVALID
+    assert f(64, 2, 128, Y, 128, P, Wt, None, G, 1e-6, RO, NO, None) == ep.EP_ERR_NULLPTR
+    assert f(64, 2, 128, Y, 128, P, Wt, R, G, 1e-6, R, NO, None) == ep.EP_ERR_INVALID   # in-place
+    assert f(64, 2, 128, Y, 128, P, Wt, R, G, 1e-6, RO, RO + 16, None) == ep.EP_ERR_INVALID
+    assert f(64, 2, 128, Y, 128, P, Wt, R, G, 1e-6, Y + 512, NO, None) == ep.EP_ERR_INVALID
+    assert f(64, 2, 128, Y, 128, P, Wt, R + 8, G, 1e-6, RO, NO, None) == ep.EP_ERR_INVALID
+    assert f(0, 2, 128, None, 0, None, None, None, None, 1e-6, None, None, None) == ep.EP_OK
+    g = ep.lib.ep_add_rmsnorm
+    assert g(64, 128, None, R, G, 1e-6, RO, NO, None) == ep.EP_ERR_NULLPTR
+    assert g(64, 128, Y, R, G, 1e-6, Y + 64, NO, None) == ep.EP_ERR_INVALID
+    assert g(0, 128, None, None, None, 1e-6, None, None, None) == ep.EP_OK
