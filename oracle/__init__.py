@@ -71,6 +71,12 @@ def _load():
     lib.oracle_plan_ex.argtypes = [i32, i32, i32, i32, P, P, P, i32, i32, i32, P, P, P, P, P, P, P,
                                    P, P, P, P]
     lib.oracle_plan_ex.restype = ctypes.c_int
+    lib.oracle_int8_encode.argtypes = [ctypes.c_float]
+    lib.oracle_int8_encode.restype = ctypes.c_int8
+    lib.oracle_dispatch_quant.argtypes = [i32, i32, i32, i32, P, P, P, P, i32, P, P, i64, P]
+    lib.oracle_dispatch_quant.restype = ctypes.c_int
+    lib.oracle_combine_quant.argtypes = [i32, i32, i32, P, i32, P, i64, P, P, P]
+    lib.oracle_combine_quant.restype = ctypes.c_int
     lib.oracle_f64_to_bf16_rne.argtypes = [ctypes.c_double]
     lib.oracle_f64_to_bf16_rne.restype = ctypes.c_uint16
     lib.oracle_combine_add_rmsnorm.argtypes = [i32, i32, i32, P, i64, P, P, P, P, ctypes.c_float, P, P]
@@ -243,6 +249,46 @@ def combine(y_bits: np.ndarray, pos: np.ndarray, weights: np.ndarray) -> np.ndar
     out = np.zeros((T, H), np.uint16)
     _check(_load().oracle_combine(T, K, H, _ptr(y_bits), cap, _ptr(pos), _ptr(weights),
                                   _ptr(out)), "combine")
+    return out
+
+
+Q_FP8 = 1
+Q_INT8 = 2
+
+
+def int8_encode(value: float) -> int:
+    return int(_load().oracle_int8_encode(float(np.float32(value))))
+
+
+def dispatch_quant(x_bits, ids, pos, E: int, qtype: int, cap_rows: int,
+                   smooth: np.ndarray | None = None, fill_q: int = 0, fill_scale: float = 0.0):
+    """Per-copy dynamic quantisation (optionally with per-expert smoothing
+    scales [E][H] fp32).  Returns (codes [cap_rows][H] uint8, scales [cap_rows])."""
+    x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    ids = np.ascontiguousarray(ids, dtype=np.int32)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    sm = None if smooth is None else np.ascontiguousarray(smooth, dtype=np.float32)
+    T, H = x_bits.shape
+    K = pos.shape[1]
+    q = np.full((cap_rows, H), fill_q, np.uint8)
+    sc = np.full(cap_rows, fill_scale, np.float32)
+    scratch = np.zeros(H, np.float32)
+    _check(_load().oracle_dispatch_quant(T, K, E, H, _ptr(x_bits), _ptr(ids), _ptr(pos), _ptr(sm),
+                                         qtype, _ptr(q), _ptr(sc), cap_rows, _ptr(scratch)),
+           "dispatch_quant")
+    return q, sc
+
+
+def combine_quant(codes, qtype: int, scales, pos, weights) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.float32)
+    pos = np.ascontiguousarray(pos, dtype=np.int32)
+    weights = np.ascontiguousarray(weights, dtype=np.float32)
+    T, K = pos.shape
+    cap, H = codes.shape
+    out = np.zeros((T, H), np.uint16)
+    _check(_load().oracle_combine_quant(T, K, H, _ptr(codes), qtype, _ptr(scales), cap, _ptr(pos),
+                                        _ptr(weights), _ptr(out)), "combine_quant")
     return out
 
 

@@ -530,6 +530,118 @@ int oracle_combine(int32_t T, int32_t K, int32_t H, const uint16_t *y,
     return ORC_OK;
 }
 
+/* ------------------------------------------------------------------ */
+/* Quantisation variants.                                              */
+/* ------------------------------------------------------------------ */
+
+#define ORC_Q_FP8 1
+#define ORC_Q_INT8 2
+
+/* int8 code of a binary32: the nearest integer, ties to the even one,
+ * clamped to [-127, 127] (symmetric per-token quantisation). */
+int8_t oracle_int8_encode(float v)
+{
+    if (isnan(v))
+        return 0;
+    if (v >= 127.0f)
+        return 127;
+    if (v <= -127.0f)
+        return -127;
+    float f = floorf(v);     /* exact: |v| < 127 */
+    float frac = v - f;      /* exact */
+    float r;
+    if (frac > 0.5f)
+        r = f + 1.0f;
+    else if (frac < 0.5f)
+        r = f;
+    else
+        r = (fmodf(f, 2.0f) == 0.0f) ? f : f + 1.0f;
+    return (int8_t)r;
+}
+
+static double orc_decode(int qtype, uint8_t code)
+{
+    return qtype == ORC_Q_FP8 ? oracle_e4m3fn_decode(code) : (double)(int8_t)code;
+}
+
+/* Dispatch with per-copy dynamic quantisation ([P4] quantMode 2: per-token
+ * dynamic quantisation, INT8 on that hardware; scalesOptional: per-expert
+ * smoothing parameters of shape (moeExpertNum, H) applied first).  For every
+ * live copy (t, k) of expert e:
+ *   xs[h]  = smooth ? fl32(x[t][h] * smooth[e][h]) : x[t][h]
+ *   amax   = max_h |xs[h]|,  scale = fl32(amax / qmax)  (qmax 448 or 127)
+ *   q[h]   = code(fl32(xs[h] / scale))  (E4M3FN RNE saturating, or int8 RNE
+ *            clamped to +-127), all codes 0 when scale == 0
+ *   expand_q[pos] = q, expand_scales[pos] = scale.
+ * Without smoothing every copy of a token carries the same row. */
+int oracle_dispatch_quant(int32_t T, int32_t K, int32_t E, int32_t H, const uint16_t *x,
+                          const int32_t *ids, const int32_t *pos, const float *smooth,
+                          int32_t qtype, uint8_t *expand_q, float *expand_scales,
+                          int64_t cap_rows, float *row_scratch)
+{
+    if (qtype != ORC_Q_FP8 && qtype != ORC_Q_INT8)
+        return ORC_ERR_ARGS;
+    const float qmax = qtype == ORC_Q_FP8 ? 448.0f : 127.0f;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k) {
+            int64_t p = pos[t * K + k];
+            if (p < 0)
+                continue;
+            if (p >= cap_rows)
+                return ORC_ERR_ARGS;
+            int32_t e = ids[t * K + k];
+            if (smooth && (e < 0 || e >= E))
+                return ORC_ERR_ARGS;
+            float amax = 0.0f;
+            for (int32_t h = 0; h < H; ++h) {
+                float v = oracle_bf16_to_f32(x[t * (int64_t)H + h]);
+                if (smooth)
+                    v = v * smooth[(int64_t)e * H + h];
+                row_scratch[h] = v;
+                if (fabsf(v) > amax)
+                    amax = fabsf(v);
+            }
+            float scale = amax / qmax;
+            for (int32_t h = 0; h < H; ++h) {
+                float v = (scale == 0.0f) ? 0.0f : row_scratch[h] / scale;
+                expand_q[p * H + h] = qtype == ORC_Q_FP8 ? oracle_e4m3fn_encode(v)
+                                                         : (uint8_t)oracle_int8_encode(v);
+            }
+            expand_scales[p] = scale;
+        }
+    }
+    return ORC_OK;
+}
+
+/* Combine reading quantised expert outputs ([P4] commQuantMode of the
+ * combine: rows travel quantised, one fp32 scale per row):
+ *   y[row][h] = fl32(decode(q[row][h]) * scales[row])
+ *   out[t][h] = bf16_rne(sum_k w[t][k] * y[pos[t][k]][h]), fp32 FMA in k order. */
+int oracle_combine_quant(int32_t T, int32_t K, int32_t H, const uint8_t *q, int32_t qtype,
+                         const float *scales, int64_t cap_rows, const int32_t *pos,
+                         const float *w, uint16_t *out)
+{
+    if (qtype != ORC_Q_FP8 && qtype != ORC_Q_INT8)
+        return ORC_ERR_ARGS;
+    for (int64_t t = 0; t < T; ++t) {
+        for (int32_t k = 0; k < K; ++k)
+            if (pos[t * K + k] >= cap_rows)
+                return ORC_ERR_ARGS;
+        for (int32_t h = 0; h < H; ++h) {
+            float acc = 0.0f;
+            for (int32_t k = 0; k < K; ++k) {
+                int64_t p = pos[t * K + k];
+                if (p < 0)
+                    continue;
+                float v = (float)orc_decode(qtype, q[p * H + h]) * scales[p];
+                acc = fmaf(w[t * K + k], v, acc);
+            }
+            out[t * (int64_t)H + h] = oracle_f32_to_bf16_rne(acc);
+        }
+    }
+    return ORC_OK;
+}
+
 /* Round a double to bf16 to nearest, ties to even, in one step (no
  * intermediate binary32 rounding). */
 uint16_t oracle_f64_to_bf16_rne(double v)
