@@ -30,6 +30,7 @@ EP_ERR_HIP = 5
 
 EP_BF16 = 0
 EP_FP8_E4M3FN = 1
+EP_INT8 = 2
 
 EP_DEVERR_BAD_EXPERT = 1
 EP_DEVERR_SPLITS = 2
@@ -40,7 +41,8 @@ _STATUS_NAMES = {1: "EP_ERR_NULLPTR", 2: "EP_ERR_INVALID", 3: "EP_ERR_UNSUPPORTE
                  4: "EP_ERR_WORKSPACE", 5: "EP_ERR_HIP"}
 
 EXPORTED = ("ep_supported", "ep_workspace_size", "ep_workspace_init", "ep_expand_rows_bound",
-            "ep_plan", "ep_dispatch", "ep_combine", "ep_combine_add_rmsnorm", "ep_add_rmsnorm",
+            "ep_plan", "ep_dispatch", "ep_dispatch_smooth", "ep_combine", "ep_combine_quant",
+            "ep_combine_add_rmsnorm", "ep_add_rmsnorm",
             "ep_plan_splits", "ep_dispatch_splits", "ep_last_error", "ep_device_error")
 
 
@@ -77,7 +79,9 @@ def _load() -> ctypes.CDLL:
         "ep_plan": ([i32, i32, i32, i32, P, P, ctypes.POINTER(_PlanOpts), ctypes.POINTER(_PlanT), P,
                      sz, P], ctypes.c_int),
         "ep_dispatch": ([i32, i32, i32, P, P, i32, P, P, P, P, i64, P], ctypes.c_int),
+        "ep_dispatch_smooth": ([i32, i32, i32, i32, P, P, P, P, i32, P, P, i64, P], ctypes.c_int),
         "ep_combine": ([i32, i32, i32, P, i64, P, P, P, P], ctypes.c_int),
+        "ep_combine_quant": ([i32, i32, i32, P, i32, P, i64, P, P, P, P], ctypes.c_int),
         "ep_combine_add_rmsnorm": ([i32, i32, i32, P, i64, P, P, P, P, ctypes.c_float, P, P, P],
                                    ctypes.c_int),
         "ep_add_rmsnorm": ([i32, i32, P, P, P, ctypes.c_float, P, P, P], ctypes.c_int),
@@ -246,6 +250,42 @@ def ep_dispatch(x: torch.Tensor, pos: torch.Tensor, expand_x: torch.Tensor,
                            _ptr(weights, torch.float32, "weights"),
                            _ptr(expand_weights, torch.float32, "expand_weights"),
                            expand_x.shape[0], _stream(stream)))
+
+
+def ep_dispatch_smooth(x: torch.Tensor, topk_ids: torch.Tensor, pos: torch.Tensor,
+                       smooth_scales: torch.Tensor, expand_x: torch.Tensor,
+                       expand_scales: torch.Tensor, out_dtype: int = EP_FP8_E4M3FN,
+                       stream=None) -> None:
+    T, H = x.shape
+    K = pos.shape[1]
+    if tuple(topk_ids.shape) != (T, K) or pos.shape[0] != T:
+        raise ValueError("topk_ids and pos must be [T][K] for x [T][H]")
+    if smooth_scales.dim() != 2 or smooth_scales.shape[1] != H:
+        raise ValueError("smooth_scales must be [E][H]")
+    if expand_x.dim() != 2 or expand_x.shape[1] != H:
+        raise ValueError("expand_x must be [cap_rows][H]")
+    _check(lib.ep_dispatch_smooth(
+        T, K, smooth_scales.shape[0], H, _ptr(x, _BITS16, "x"),
+        _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(pos, torch.int32, "pos"),
+        _ptr(smooth_scales, torch.float32, "smooth_scales"), out_dtype,
+        _ptr(expand_x, _BITS8, "expand_x"), _ptr(expand_scales, torch.float32, "expand_scales"),
+        expand_x.shape[0], _stream(stream)))
+
+
+def ep_combine_quant(codes: torch.Tensor, row_scales: torch.Tensor, pos: torch.Tensor,
+                     weights: torch.Tensor, out: torch.Tensor, code_dtype: int = EP_FP8_E4M3FN,
+                     stream=None) -> None:
+    T, K = pos.shape
+    cap, H = codes.shape
+    if tuple(out.shape) != (T, H) or tuple(weights.shape) != (T, K):
+        raise ValueError("out must be [T][H] and weights [T][K]")
+    if row_scales.numel() < cap:
+        raise ValueError("row_scales must hold one scale per row of codes")
+    _check(lib.ep_combine_quant(T, K, H, _ptr(codes, _BITS8, "codes"), code_dtype,
+                                _ptr(row_scales, torch.float32, "row_scales"), cap,
+                                _ptr(pos, torch.int32, "pos"),
+                                _ptr(weights, torch.float32, "weights"),
+                                _ptr(out, _BITS16, "out"), _stream(stream)))
 
 
 def ep_combine(y: torch.Tensor, pos: torch.Tensor, weights: torch.Tensor, out: torch.Tensor,

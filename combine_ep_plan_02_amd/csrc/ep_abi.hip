@@ -14,6 +14,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <mutex>
+#include <type_traits>
 #include <string>
 #include <unordered_map>
 
@@ -60,6 +61,11 @@ int ok() {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
+struct Range_ {
+  const void* p;
+  size_t n;
+};
+
 // [a, a+na) and [b, b+nb) share a byte.
 bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   if (!a || !b || na == 0 || nb == 0) return false;
@@ -85,7 +91,8 @@ int check_dims(int32_t T, int32_t K, int32_t E, int32_t W) {
 }
 
 int check_rows(int32_t H, int32_t dtype) {
-  if (dtype != EP_BF16 && dtype != EP_FP8_E4M3FN) return fail(EP_ERR_INVALID, "unknown row dtype %d", dtype);
+  if (dtype != EP_BF16 && dtype != EP_FP8_E4M3FN && dtype != EP_INT8)
+    return fail(EP_ERR_INVALID, "unknown row dtype %d", dtype);
   if (H < 1 || H > EP_MAX_H) return fail(EP_ERR_UNSUPPORTED, "H must be in [1, %d] (got %d)", EP_MAX_H, H);
   const int vec = dtype == EP_BF16 ? 8 : 16;
   if (H % vec) return fail(EP_ERR_UNSUPPORTED, "H (%d) must be a multiple of %d for this row dtype", H, vec);
@@ -312,8 +319,8 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
                 (long long)T * K);
   if (T == 0) return ok();
   if (!x || !pos || !expand_x) return fail(EP_ERR_NULLPTR, "x, pos and expand_x are required");
-  const bool fp8 = out_dtype == EP_FP8_E4M3FN;
-  if (fp8 && !expand_scales) return fail(EP_ERR_NULLPTR, "expand_scales is required for fp8 rows");
+  const bool fp8 = out_dtype != EP_BF16;  // quantised rows: fp8 or int8 codes + scales
+  if (fp8 && !expand_scales) return fail(EP_ERR_NULLPTR, "expand_scales is required for quantised rows");
   if (!aligned(x, 16) || !aligned(expand_x, 16))
     return fail(EP_ERR_INVALID, "x and expand_x must be 16-byte aligned");
   if (!aligned(pos, 4) || (fp8 && !aligned(expand_scales, 4)))
@@ -356,19 +363,20 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
   ep::u32x4* qv = (ep::u32x4*)expand_x;
   const dim3 tgrid((unsigned)T);  // one workgroup per token
   const int per_thread = (NG + ep::kRowThreads - 1) / ep::kRowThreads;
-  if (per_thread <= 1)
-    hipLaunchKernelGGL((ep::dispatch_fp8_kernel<1, kFp8NtLoad, kFp8NtStore>), tgrid, block, 0, s, xv, pos, qv,
-                       expand_scales, weights, expand_weights, T, K, NG, cap_rows);
-  else if (per_thread <= 2)
-    hipLaunchKernelGGL((ep::dispatch_fp8_kernel<2, kFp8NtLoad, kFp8NtStore>), tgrid, block, 0, s, xv, pos, qv,
-                       expand_scales, weights, expand_weights, T, K, NG, cap_rows);
-  else if (per_thread <= 4)
-    hipLaunchKernelGGL((ep::dispatch_fp8_kernel<4, kFp8NtLoad, kFp8NtStore>), tgrid, block, 0, s, xv, pos, qv,
-                       expand_scales, weights, expand_weights, T, K, NG, cap_rows);
-  else
-    hipLaunchKernelGGL((ep::dispatch_fp8_kernel<8, kFp8NtLoad, kFp8NtStore>), tgrid, block, 0, s, xv, pos, qv,
-                       expand_scales, weights, expand_weights, T, K, NG, cap_rows);
-  return launch_status("ep_dispatch (fp8)");
+  auto launch = [&](auto qt) {
+    constexpr int QT = decltype(qt)::value;
+#define EP_QDISP(G)                                                                                          \
+  hipLaunchKernelGGL((ep::dispatch_quant_kernel<QT, G, kFp8NtLoad, kFp8NtStore>), tgrid, block, 0, s, xv, pos, qv, \
+                     expand_scales, weights, expand_weights, T, K, NG, cap_rows)
+    if (per_thread <= 1) EP_QDISP(1);
+    else if (per_thread <= 2) EP_QDISP(2);
+    else if (per_thread <= 4) EP_QDISP(4);
+    else EP_QDISP(8);
+#undef EP_QDISP
+  };
+  if (out_dtype == EP_FP8_E4M3FN) launch(std::integral_constant<int, ep::kQFp8>{});
+  else launch(std::integral_constant<int, ep::kQInt8>{});
+  return launch_status("ep_dispatch (quantised rows)");
 }
 
 EP_EXPORT int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t* y, int64_t cap_rows,
@@ -408,6 +416,105 @@ EP_EXPORT int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t* y, int
     hipLaunchKernelGGL((ep::combine_kernel<16, kCombineUnroll, kCombineNtLoad, kCombineNtStore>), cgrid, block, 0,
                        s, yv, pos, weights, ov, T, K, V, chunks, cap_rows);
   return launch_status("ep_combine");
+}
+
+constexpr int kSmoothMaxH = 16384;  // 4 groups of 16 values per thread stay in VGPRs
+
+EP_EXPORT int ep_dispatch_smooth(int32_t T, int32_t K, int32_t E, int32_t H, const uint16_t* x,
+                                 const int32_t* topk_ids, const int32_t* pos, const float* smooth_scales,
+                                 int32_t out_dtype, void* expand_x, float* expand_scales, int64_t cap_rows,
+                                 void* stream) {
+  if (T < 0) return fail(EP_ERR_INVALID, "T must be >= 0 (got %d)", T);
+  if (K < 1 || K > EP_MAX_K) return fail(EP_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)", EP_MAX_K, K);
+  if (E < 1 || E > EP_MAX_E) return fail(EP_ERR_UNSUPPORTED, "E must be in [1, %d] (got %d)", EP_MAX_E, E);
+  if (out_dtype != EP_FP8_E4M3FN && out_dtype != EP_INT8)
+    return fail(EP_ERR_INVALID, "smoothing quantises to fp8 or int8 rows (got dtype %d)", out_dtype);
+  int rc = check_rows(H, out_dtype);
+  if (rc) return rc;
+  if (H > kSmoothMaxH) return fail(EP_ERR_UNSUPPORTED, "H must be <= %d with smoothing (got %d)", kSmoothMaxH, H);
+  if ((int64_t)T * K >= (int64_t)1 << 31) return fail(EP_ERR_UNSUPPORTED, "T*K must be < 2^31");
+  if (cap_rows < (int64_t)T * K)
+    return fail(EP_ERR_INVALID, "cap_rows (%lld) must be >= T*K", (long long)cap_rows);
+  if (T == 0) return ok();
+  if (!x || !topk_ids || !pos || !smooth_scales || !expand_x || !expand_scales)
+    return fail(EP_ERR_NULLPTR, "x, topk_ids, pos, smooth_scales, expand_x and expand_scales are required");
+  if (!aligned(x, 16) || !aligned(expand_x, 16) || !aligned(smooth_scales, 16))
+    return fail(EP_ERR_INVALID, "x, expand_x and smooth_scales must be 16-byte aligned");
+  if (!aligned(topk_ids, 4) || !aligned(pos, 4) || !aligned(expand_scales, 4))
+    return fail(EP_ERR_INVALID, "topk_ids, pos and expand_scales must be 4-byte aligned");
+  const size_t eb = (size_t)cap_rows * H, sb = (size_t)cap_rows * 4;
+  const Range_ ins[] = {{x, (size_t)T * H * 2}, {topk_ids, (size_t)T * K * 4}, {pos, (size_t)T * K * 4},
+                        {smooth_scales, (size_t)E * H * 4}};
+  for (const auto& r : ins)
+    if (overlap(expand_x, eb, r.p, r.n) || overlap(expand_scales, sb, r.p, r.n))
+      return fail(EP_ERR_INVALID, "an output overlaps an input");
+  if (overlap(expand_x, eb, expand_scales, sb)) return fail(EP_ERR_INVALID, "expand_x overlaps expand_scales");
+  const int NG = H / 16;
+  const int per_thread = (NG + ep::kRowThreads - 1) / ep::kRowThreads;
+  hipStream_t s = (hipStream_t)stream;
+  const ep::u32x4* xv = (const ep::u32x4*)x;
+  const float4* sm = (const float4*)smooth_scales;
+  ep::u32x4* qv = (ep::u32x4*)expand_x;
+  auto launch = [&](auto qt) {
+    constexpr int QT = decltype(qt)::value;
+#define EP_SMOOTH(G)                                                                                      \
+  hipLaunchKernelGGL((ep::dispatch_smooth_kernel<QT, G, kFp8NtStore>), dim3((unsigned)T), dim3(ep::kRowThreads), \
+                     0, s, xv, topk_ids, pos, sm, qv, expand_scales, T, K, E, NG, cap_rows)
+    if (per_thread <= 1) EP_SMOOTH(1);
+    else if (per_thread <= 2) EP_SMOOTH(2);
+    else EP_SMOOTH(4);
+#undef EP_SMOOTH
+  };
+  if (out_dtype == EP_FP8_E4M3FN) launch(std::integral_constant<int, ep::kQFp8>{});
+  else launch(std::integral_constant<int, ep::kQInt8>{});
+  return launch_status("ep_dispatch_smooth");
+}
+
+EP_EXPORT int ep_combine_quant(int32_t T, int32_t K, int32_t H, const void* codes, int32_t code_dtype,
+                               const float* row_scales, int64_t cap_rows, const int32_t* pos,
+                               const float* weights, uint16_t* out, void* stream) {
+  if (T < 0) return fail(EP_ERR_INVALID, "T must be >= 0 (got %d)", T);
+  if (K < 1 || K > EP_MAX_K) return fail(EP_ERR_UNSUPPORTED, "K must be in [1, %d] (got %d)", EP_MAX_K, K);
+  if (code_dtype != EP_FP8_E4M3FN && code_dtype != EP_INT8)
+    return fail(EP_ERR_INVALID, "codes must be fp8 or int8 (got dtype %d)", code_dtype);
+  int rc = check_rows(H, code_dtype);
+  if (rc) return rc;
+  if ((int64_t)T * K >= (int64_t)1 << 31) return fail(EP_ERR_UNSUPPORTED, "T*K must be < 2^31");
+  if (cap_rows < 0) return fail(EP_ERR_INVALID, "cap_rows must be >= 0");
+  if (T == 0) return ok();
+  if (!codes || !row_scales || !pos || !weights || !out)
+    return fail(EP_ERR_NULLPTR, "codes, row_scales, pos, weights and out are required");
+  if (!aligned(codes, 16) || !aligned(out, 16)) return fail(EP_ERR_INVALID, "codes and out must be 16-byte aligned");
+  if (!aligned(row_scales, 4) || !aligned(pos, 4) || !aligned(weights, 4))
+    return fail(EP_ERR_INVALID, "row_scales, pos and weights must be 4-byte aligned");
+  const size_t ob = (size_t)T * H * 2;
+  if (overlap(out, ob, codes, (size_t)cap_rows * H) || overlap(out, ob, row_scales, (size_t)cap_rows * 4) ||
+      overlap(out, ob, pos, (size_t)T * K * 4) || overlap(out, ob, weights, (size_t)T * K * 4))
+    return fail(EP_ERR_INVALID, "out overlaps an input");
+  const int NG = H / 16;
+  const int chunks = (NG + ep::kWave - 1) / ep::kWave;
+  const int64_t items = (int64_t)T * chunks;
+  if ((items + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock > INT32_MAX)
+    return fail(EP_ERR_UNSUPPORTED, "T * H too large for one launch");
+  const dim3 grid((unsigned)((items + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock)), block(ep::kRowThreads);
+  hipStream_t s = (hipStream_t)stream;
+  const ep::u32x4* cv = (const ep::u32x4*)codes;
+  ep::u32x4* ov = (ep::u32x4*)out;
+  auto launch = [&](auto qt) {
+    constexpr int QT = decltype(qt)::value;
+    if (K <= 4)
+      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 4, kCombineNtLoad, kCombineNtStore>), grid, block, 0, s, cv,
+                         row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
+    else if (K <= 8)
+      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 8, kCombineNtLoad, kCombineNtStore>), grid, block, 0, s, cv,
+                         row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
+    else
+      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 16, kCombineNtLoad, kCombineNtStore>), grid, block, 0, s, cv,
+                         row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
+  };
+  if (code_dtype == EP_FP8_E4M3FN) launch(std::integral_constant<int, ep::kQFp8>{});
+  else launch(std::integral_constant<int, ep::kQInt8>{});
+  return launch_status("ep_combine_quant");
 }
 
 namespace {

@@ -113,24 +113,59 @@ __device__ __forceinline__ uint32_t e4m3fn_code(float v) {
   return sign | mag;
 }
 
-// Quantise 16 bf16 values (two 16-byte vectors) into 16 codes.
-__device__ __forceinline__ u32x4 quantize16(const u32x4 a, const u32x4 b, float scale) {
-  uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+// int8 code: nearest integer, ties to even (v_rndne), clamped to +-127.
+__device__ __forceinline__ uint32_t int8_code(float v) {
+  float r = __builtin_rintf(v);
+  r = fminf(fmaxf(r, -127.0f), 127.0f);
+  return (uint32_t)((int32_t)r) & 0xffu;
+}
+
+constexpr int kQFp8 = 1;
+constexpr int kQInt8 = 2;
+
+template <int QT>
+__device__ __forceinline__ uint32_t quant_code(float v) {
+  if constexpr (QT == kQFp8) return e4m3fn_code(v);
+  else return int8_code(v);
+}
+
+template <int QT>
+__device__ __forceinline__ float quant_max() {
+  if constexpr (QT == kQFp8) return 448.0f;
+  else return 127.0f;
+}
+
+// Quantise 16 fp32 values into 16 codes (zero codes when scale == 0).
+template <int QT>
+__device__ __forceinline__ u32x4 quantize16f(const float* f, float scale) {
   uint32_t out[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const uint32_t lo = w[2 * i], hi = w[2 * i + 1];
-    const float f0 = bf16lo(lo), f1 = bf16hi(lo), f2 = bf16lo(hi), f3 = bf16hi(hi);
-    uint32_t c0 = 0, c1 = 0, c2 = 0, c3 = 0;
+    uint32_t c[4] = {0, 0, 0, 0};
     if (scale != 0.0f) {
-      c0 = e4m3fn_code(f0 / scale);
-      c1 = e4m3fn_code(f1 / scale);
-      c2 = e4m3fn_code(f2 / scale);
-      c3 = e4m3fn_code(f3 / scale);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) c[j] = quant_code<QT>(f[4 * i + j] / scale);
     }
-    out[i] = c0 | (c1 << 8) | (c2 << 16) | (c3 << 24);
+    out[i] = c[0] | (c[1] << 8) | (c[2] << 16) | (c[3] << 24);
   }
   return u32x4{out[0], out[1], out[2], out[3]};
+}
+
+__device__ __forceinline__ void unpack16(const u32x4 a, const u32x4 b, float* f) {
+  const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    f[2 * i] = bf16lo(w[i]);
+    f[2 * i + 1] = bf16hi(w[i]);
+  }
+}
+
+// Quantise 16 bf16 values (two 16-byte vectors) into 16 codes.
+template <int QT>
+__device__ __forceinline__ u32x4 quantize16(const u32x4 a, const u32x4 b, float scale) {
+  float f[16];
+  unpack16(a, b, f);
+  return quantize16f<QT>(f, scale);
 }
 
 // Largest bf16 magnitude of two vectors, as the 15-bit magnitude pattern
@@ -149,8 +184,8 @@ __device__ __forceinline__ uint32_t amax16_bits(const u32x4 a, const u32x4 b, ui
 // i, i + 256, ...; the first G of them stay in VGPRs between the amax pass and
 // the quantise pass, longer rows re-read the rest.  The row's amax is
 // reduced across lanes with shuffles and across the 4 waves through LDS.
-template <int G, bool NTL, bool NTS>
-__global__ __launch_bounds__(kRowThreads) void dispatch_fp8_kernel(
+template <int QT, int G, bool NTL, bool NTS>
+__global__ __launch_bounds__(kRowThreads) void dispatch_quant_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ pos, u32x4* __restrict__ q,
     float* __restrict__ scales, const float* __restrict__ weights,
     float* __restrict__ expand_weights, int T, int K, int NG, int64_t cap_rows) {
@@ -185,13 +220,13 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_fp8_kernel(
 #pragma unroll
   for (int w = 1; w < kRowThreads / kWave; ++w) m = max(m, s_max[w]);
   const float amax = __uint_as_float(m << 16);
-  const float scale = amax / 448.0f;
+  const float scale = amax / quant_max<QT>();
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int idx = g * kRowThreads + tid;
     if (idx < NG) {
-      const u32x4 code = quantize16(cache[g][0], cache[g][1], scale);
+      const u32x4 code = quantize16<QT>(cache[g][0], cache[g][1], scale);
       uint64_t mk = live;
       while (mk) {
         const int k = __builtin_ctzll(mk);
@@ -202,7 +237,7 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_fp8_kernel(
     }
   }
   for (int idx = G * kRowThreads + tid; idx < NG; idx += kRowThreads) {
-    const u32x4 code = quantize16(ld<NTL>(src + 2 * idx), ld<NTL>(src + 2 * idx + 1), scale);
+    const u32x4 code = quantize16<QT>(ld<NTL>(src + 2 * idx), ld<NTL>(src + 2 * idx + 1), scale);
     uint64_t mk = live;
     while (mk) {
       const int k = __builtin_ctzll(mk);
@@ -289,6 +324,160 @@ __global__ __launch_bounds__(kRowThreads) void combine_kernel(
       st<NTS>(dst + idx, o);
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Dispatch with per-expert smoothing before per-copy dynamic quantisation
+// (scalesOptional of shape (E, H) with quantMode 2 on the CANN dispatch
+// page): for every live copy (t, k) of expert e, xs = fl32(x[t] * smooth[e]),
+// scale = fl32(max|xs| / qmax), codes of fl32(xs / scale).  Each copy gets
+// its own row and scale.  One workgroup per token; the token's row stays in
+// VGPRs (as bf16) while the copies are quantised one after another, each
+// copy's smoothing row read from L2 (E x H fp32 is shared by all tokens).
+// ---------------------------------------------------------------------------
+template <int QT, int G, bool NTS>
+__global__ __launch_bounds__(kRowThreads) void dispatch_smooth_kernel(
+    const u32x4* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ pos,
+    const float4* __restrict__ smooth, u32x4* __restrict__ q, float* __restrict__ scales, int T, int K,
+    int E, int NG, int64_t cap_rows) {
+  __shared__ uint32_t s_max[kRowThreads / kWave];
+  const int t = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = lane_id();
+  const int wave = tid / kWave;
+  const int my_pos = row_of(pos, t, K, lane, cap_rows);
+  const int my_e = lane < K ? ids[(int64_t)t * K + lane] : -1;
+  const uint64_t live = ballot(my_pos >= 0 && (unsigned)my_e < (unsigned)E);
+  if (ballot(my_pos >= 0 && (unsigned)my_e >= (unsigned)E) && lane == 0) raise_device_error(kErrBadExpert);
+  if (live == 0) return;
+  const u32x4* src = x + (int64_t)t * NG * 2;
+  u32x4 xr[G][2];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    const int idx = g * kRowThreads + tid;
+    if (idx < NG) {
+      xr[g][0] = src[2 * idx];
+      xr[g][1] = src[2 * idx + 1];
+    }
+  }
+  uint64_t mk = live;
+  while (mk) {
+    const int k = __builtin_ctzll(mk);
+    mk &= mk - 1;
+    const int p = __builtin_amdgcn_readlane(my_pos, k);
+    const int e = __builtin_amdgcn_readlane(my_e, k);
+    const float4* srow = smooth + (int64_t)e * NG * 4;
+    float xs[G][16];
+    float amax = 0.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int idx = g * kRowThreads + tid;
+      if (idx < NG) {
+        float f[16];
+        unpack16(xr[g][0], xr[g][1], f);
+#pragma unroll
+        for (int qd = 0; qd < 4; ++qd) {
+          const float4 sv = srow[4 * idx + qd];
+          xs[g][4 * qd + 0] = f[4 * qd + 0] * sv.x;
+          xs[g][4 * qd + 1] = f[4 * qd + 1] * sv.y;
+          xs[g][4 * qd + 2] = f[4 * qd + 2] * sv.z;
+          xs[g][4 * qd + 3] = f[4 * qd + 3] * sv.w;
+        }
+#pragma unroll
+        for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(xs[g][j]));
+      }
+    }
+    uint32_t mb = __float_as_uint(amax);
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, kWave));
+    __syncthreads();  // the previous copy's reads of s_max are done
+    if (lane == 0) s_max[wave] = mb;
+    __syncthreads();
+    uint32_t m = s_max[0];
+#pragma unroll
+    for (int w = 1; w < kRowThreads / kWave; ++w) m = max(m, s_max[w]);
+    const float scale = __uint_as_float(m) / quant_max<QT>();
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      const int idx = g * kRowThreads + tid;
+      if (idx < NG) st<NTS>(q + (int64_t)p * NG + idx, quantize16f<QT>(xs[g], scale));
+    }
+    if (tid == 0) scales[p] = scale;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Combine of quantised expert rows (commQuantMode of the CANN combine): row
+// values are decode(code) * row_scale in fp32, then summed with the gate
+// weights as ep_combine does.  Work item: one wavefront per (token, chunk of
+// 1024 columns); a lane reads 16 codes (16 bytes) of each of the K rows.
+// ---------------------------------------------------------------------------
+template <int QT>
+__device__ __forceinline__ float decode_code(uint32_t c) {
+  if constexpr (QT == kQInt8) {
+    return (float)(int32_t)(int8_t)(c & 0xffu);
+  } else {
+    const uint32_t sign = (c & 0x80u) << 24;
+    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
+    if (e == 0) return __uint_as_float(sign | __float_as_uint((float)m * 0.001953125f));  // m * 2^-9
+    if (e == 15 && m == 7) return __uint_as_float(0x7fc00000u);
+    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+  }
+}
+
+template <int QT, int KMAX, bool NTL, bool NTS>
+__global__ __launch_bounds__(kRowThreads) void combine_quant_kernel(
+    const u32x4* __restrict__ codes, const float* __restrict__ row_scales,
+    const int32_t* __restrict__ pos, const float* __restrict__ w, u32x4* __restrict__ out, int T,
+    int K, int NG, int chunks, int64_t cap_rows) {
+  const int64_t g = (int64_t)blockIdx.x * kTokensPerBlock + uniform((int)(threadIdx.x / kWave));
+  const int64_t t64 = g / chunks;
+  if (t64 >= T) return;
+  const int t = (int)t64;
+  const int idx = (int)(g - t64 * chunks) * kWave + lane_id();
+  const int lane = lane_id();
+  const int my_pos = row_of(pos, t, K, lane, cap_rows);
+  const float my_w = lane < K ? w[(int64_t)t * K + lane] : 0.0f;
+  const float my_s = my_pos >= 0 ? row_scales[my_pos] : 0.0f;
+  int pk[KMAX];
+  float wk[KMAX], sk[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    pk[k] = __builtin_amdgcn_readlane(my_pos, k);
+    wk[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_w), k));
+    sk[k] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(my_s), k));
+  }
+  if (idx >= NG) return;
+  u32x4 r[KMAX];
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k)
+    if (pk[k] >= 0) r[k] = ld<NTL>(codes + (int64_t)pk[k] * NG + idx);
+  float acc[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) acc[j] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < KMAX; ++k) {
+    if (pk[k] >= 0) {
+      const uint32_t c4[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const float v = decode_code<QT>(c4[j / 4] >> (8 * (j % 4))) * sk[k];
+        acc[j] = __builtin_fmaf(wk[k], v, acc[j]);
+      }
+    }
+  }
+  u32x4 o0, o1;
+  o0.x = f32_to_bf16_rne(acc[0]) | (f32_to_bf16_rne(acc[1]) << 16);
+  o0.y = f32_to_bf16_rne(acc[2]) | (f32_to_bf16_rne(acc[3]) << 16);
+  o0.z = f32_to_bf16_rne(acc[4]) | (f32_to_bf16_rne(acc[5]) << 16);
+  o0.w = f32_to_bf16_rne(acc[6]) | (f32_to_bf16_rne(acc[7]) << 16);
+  o1.x = f32_to_bf16_rne(acc[8]) | (f32_to_bf16_rne(acc[9]) << 16);
+  o1.y = f32_to_bf16_rne(acc[10]) | (f32_to_bf16_rne(acc[11]) << 16);
+  o1.z = f32_to_bf16_rne(acc[12]) | (f32_to_bf16_rne(acc[13]) << 16);
+  o1.w = f32_to_bf16_rne(acc[14]) | (f32_to_bf16_rne(acc[15]) << 16);
+  u32x4* dst = out + (int64_t)t * NG * 2;
+  st<NTS>(dst + 2 * idx, o0);
+  st<NTS>(dst + 2 * idx + 1, o1);
 }
 
 // ---------------------------------------------------------------------------

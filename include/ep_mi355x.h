@@ -52,7 +52,8 @@ typedef enum {
 
 typedef enum {
     EP_BF16 = 0,       /* expandX rows are bf16, bit copies of x           */
-    EP_FP8_E4M3FN = 1  /* expandX rows are OCP E4M3FN codes + fp32 scales  */
+    EP_FP8_E4M3FN = 1, /* expandX rows are OCP E4M3FN codes + fp32 scales  */
+    EP_INT8 = 2        /* expandX rows are int8 codes + fp32 scales        */
 } ep_dtype;
 
 /* Device error bits (ep_device_error). */
@@ -180,7 +181,8 @@ int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t *topk_ids,
  *                  expand_x[pos][h] = E4M3FN_rne_sat(fl32(x[t][h] / scale))
  *                  (all codes 0x00 when scale == 0), expand_scales[pos] = scale
  *                  (dynamicScalesOut: one fp32 scale per expanded row).
- * x [T][H] bf16; expand_x [cap_rows][H] (uint16 bf16 or uint8 codes);
+ * x [T][H] bf16; expand_x [cap_rows][H] (uint16 bf16, or uint8 codes; H % 16
+ * for codes);
  * expand_scales [cap_rows] fp32, required for fp8, ignored for bf16.
  * weights [T][K] fp32 and expand_weights [cap_rows] fp32, both or neither:
  * expand_weights[pos[t][k]] = weights[t][k], the gate weight carried to each
@@ -204,6 +206,32 @@ int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t *x, const int32_
  * pos must be < cap_rows (ep_plan guarantees it). */
 int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t *y, int64_t cap_rows,
                const int32_t *pos, const float *weights, uint16_t *out, void *stream);
+
+/* Dispatch with per-expert smoothing before per-copy dynamic quantisation
+ * (scalesOptional, shape (E, H), with quantMode 2 on the CANN dispatch
+ * page).  For every live copy (t,k) of expert e = topk_ids[t][k]:
+ *   xs[h] = fl32(x[t][h] * smooth_scales[e][h]),
+ *   scale = fl32(max_h |xs[h]| / qmax)  (qmax 448 for EP_FP8_E4M3FN, 127 for
+ *   EP_INT8), expand_x[pos][h] = code(fl32(xs[h] / scale)) (zero codes when
+ *   scale == 0), expand_scales[pos] = scale.
+ * Each copy gets its own row and scale.  smooth_scales [E][H] fp32 16-byte
+ * aligned; 16 <= H <= 16384, H % 16 == 0; cap_rows >= T*K.  A live copy whose
+ * id is outside [0, E) is skipped and raises EP_DEVERR_BAD_EXPERT. */
+int ep_dispatch_smooth(int32_t T, int32_t K, int32_t E, int32_t H, const uint16_t *x,
+                       const int32_t *topk_ids, const int32_t *pos, const float *smooth_scales,
+                       int32_t out_dtype, void *expand_x, float *expand_scales, int64_t cap_rows,
+                       void *stream);
+
+/* Combine of quantised expert rows (commQuantMode of the CANN combine: rows
+ * travel as codes with one fp32 scale per row):
+ *   y[row][h] = fl32(decode(codes[row][h]) * row_scales[row])
+ *   out[t][h] = bf16_rne(sum over live k of w[t][k] * y[pos[t][k]][h]),
+ * fp32 fused multiply-adds in increasing k from +0, as ep_combine.
+ * codes [cap_rows][H] uint8 (E4M3FN or int8 per code_dtype), row_scales
+ * [cap_rows] fp32, out [T][H] bf16; H % 16 == 0. */
+int ep_combine_quant(int32_t T, int32_t K, int32_t H, const void *codes, int32_t code_dtype,
+                     const float *row_scales, int64_t cap_rows, const int32_t *pos,
+                     const float *weights, uint16_t *out, void *stream);
 
 /* Combine fused with the layer tail (the MoE-finalize + residual + RMSNorm
  * pattern of flashinfer PR #4358 without its all-reduce; CombineAddRmsNorm

@@ -216,3 +216,39 @@ def test_tail_rejections(ep):
     assert g(64, 128, None, R, G, 1e-6, RO, NO, None) == ep.EP_ERR_NULLPTR
     assert g(64, 128, Y, R, G, 1e-6, Y + 64, NO, None) == ep.EP_ERR_INVALID
     assert g(0, 128, None, None, None, 1e-6, None, None, None) == ep.EP_OK
+
+
+def test_int8_rows_supported(ep):
+    assert ep.ep_supported(4096, 8, 256, 16, 7168, ep.EP_INT8)
+    assert not ep.ep_supported(64, 2, 8, 2, 136, ep.EP_INT8)  # H % 16
+
+
+def test_dispatch_smooth_rejections(ep):
+    d = ep.lib.ep_dispatch_smooth
+    X, I, P, SM, EX, S = A, A + (1 << 33), A + (1 << 34), A + (1 << 35), A + (1 << 36), A + (1 << 37)
+    F8, I8 = ep.EP_FP8_E4M3FN, ep.EP_INT8
+    assert d(64, 2, 8, 128, X, I, P, SM, ep.EP_BF16, EX, S, 128, None) == ep.EP_ERR_INVALID  # needs codes
+    assert d(64, 2, 8, 136, X, I, P, SM, I8, EX, S, 128, None) == ep.EP_ERR_UNSUPPORTED      # H % 16
+    assert d(64, 2, 8, 16400, X, I, P, SM, F8, EX, S, 128, None) == ep.EP_ERR_UNSUPPORTED    # H > 16384
+    assert d(64, 2, 0, 128, X, I, P, SM, F8, EX, S, 128, None) == ep.EP_ERR_UNSUPPORTED      # E < 1
+    assert d(64, 2, 8, 128, X, I, P, SM, F8, EX, S, 127, None) == ep.EP_ERR_INVALID          # cap < T*K
+    assert d(64, 2, 8, 128, X, I, P, None, F8, EX, S, 128, None) == ep.EP_ERR_NULLPTR
+    assert d(64, 2, 8, 128, X, I, P, SM, F8, EX, None, 128, None) == ep.EP_ERR_NULLPTR
+    assert d(64, 2, 8, 128, X, I, P, SM + 4, F8, EX, S, 128, None) == ep.EP_ERR_INVALID       # alignment
+    assert d(64, 2, 8, 128, X, I, P, SM, F8, SM + 256, S, 128, None) == ep.EP_ERR_INVALID     # out over smooth
+    assert d(64, 2, 8, 128, X, I, P, SM, F8, EX, EX + 64, 128, None) == ep.EP_ERR_INVALID     # out over out
+    assert d(0, 2, 8, 128, None, None, None, None, F8, None, None, 0, None) == ep.EP_OK
+
+
+def test_combine_quant_rejections(ep):
+    c = ep.lib.ep_combine_quant
+    Q, S, P, Wt, O = A, A + (1 << 33), A + (1 << 34), A + (1 << 35), A + (1 << 36)
+    F8, I8 = ep.EP_FP8_E4M3FN, ep.EP_INT8
+    assert c(64, 2, 128, Q, ep.EP_BF16, S, 128, P, Wt, O, None) == ep.EP_ERR_INVALID
+    assert c(64, 2, 136, Q, I8, S, 128, P, Wt, O, None) == ep.EP_ERR_UNSUPPORTED
+    assert c(64, 17, 128, Q, F8, S, 128, P, Wt, O, None) == ep.EP_ERR_UNSUPPORTED
+    assert c(64, 2, 128, Q, F8, None, 128, P, Wt, O, None) == ep.EP_ERR_NULLPTR
+    assert c(64, 2, 128, Q + 8, F8, S, 128, P, Wt, O, None) == ep.EP_ERR_INVALID
+    assert c(64, 2, 128, Q, F8, S, 128, P, Wt, Q + 512, None) == ep.EP_ERR_INVALID  # out over codes
+    assert c(64, 2, 128, Q, F8, S, -1, P, Wt, O, None) == ep.EP_ERR_INVALID
+    assert c(0, 2, 128, None, F8, None, 0, None, None, None, None) == ep.EP_OK

@@ -151,6 +151,13 @@ def expert_outputs(n_rows: int, H: int, seed: int) -> np.ndarray:
     return normal_bf16(np.random.default_rng(seed + 1000), (n_rows, H), 1.0)
 
 
+def smooth_scales(E: int, H: int, seed: int) -> np.ndarray:
+    """Per-expert smoothing scales [E][H] fp32: log-normal around 1 (spread
+    e^0.5), the range of per-channel activation smoothing factors."""
+    rng = np.random.default_rng(seed + 2000)
+    return np.exp(0.5 * rng.standard_normal((E, H))).astype(np.float32)
+
+
 def send_matrix(cfg: SplitsConfig) -> np.ndarray:
     rng = np.random.default_rng(cfg.seed)
     a = rng.integers(0, 1024, size=(cfg.W, cfg.W)).astype(np.int64)
