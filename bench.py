@@ -123,6 +123,14 @@ class MoEBench:
             self.gamma = (1 + 0.1 * t.randn(cfg.H, generator=g, device=dev)).to(t.bfloat16).view(t.int16)
             self.res_out = t.empty((cfg.T, cfg.H), dtype=t.int16, device=dev)
             self.norm_out = t.empty((cfg.T, cfg.H), dtype=t.int16, device=dev)
+        # the quantisation variants timed beside the step: smoothed fp8
+        # dispatch (per-expert scales [E][H]) and the combine of fp8 expert rows
+        self.smooth = t.from_numpy(workloads.smooth_scales(cfg.E, cfg.H, cfg.seed)).to(dev)
+        if cfg.fp8:
+            self.qx, self.qs = self.ex, self.scales
+        else:
+            self.qx = t.empty((cap, cfg.H), dtype=t.uint8, device=dev)
+            self.qs = t.empty(cap, dtype=t.float32, device=dev)
         # sizes for the byte accounting
         live_tok = cfg.T if inp.active is None else int(inp.active.sum())
         self.live_tokens = live_tok
@@ -144,16 +152,28 @@ class MoEBench:
         self.ep.ep_add_rmsnorm(self.out, self.residual, self.gamma, 1e-6, self.res_out,
                                self.norm_out)
 
+    def dispatch_smooth_step(self):
+        self.ep.ep_dispatch_smooth(self.x, self.ids, self.plan.pos, self.smooth, self.qx, self.qs,
+                                   out_dtype=self.ep.EP_FP8_E4M3FN)
+
+    def combine_quant_step(self):
+        self.ep.ep_combine_quant(self.qx, self.qs, self.plan.pos, self.w, self.out,
+                                 code_dtype=self.ep.EP_FP8_E4M3FN)
+
     def phases(self):
         last = ("ep_combine_add_rmsnorm", self.tail_step) if self.tail else \
             ("ep_combine", self.combine_step)
         return [("ep_plan", self.plan_step), ("ep_dispatch", self.dispatch_step), last]
 
     def extra_phases(self):
-        """Kernels timed beside the step: the unfused tail pair."""
-        if not self.tail:
-            return []
-        return [("ep_combine", self.combine_step), ("ep_add_rmsnorm", self.add_rmsnorm_step)]
+        """Kernels timed beside the step: the quantisation variants (smoothed
+        fp8 dispatch, combine of fp8 expert rows) and, with the tail, the
+        unfused tail pair."""
+        ph = [("ep_dispatch_smooth", self.dispatch_smooth_step),
+              ("ep_combine_quant", self.combine_quant_step)]
+        if self.tail:
+            ph += [("ep_combine", self.combine_step), ("ep_add_rmsnorm", self.add_rmsnorm_step)]
+        return ph
 
     def n_rows(self):
         return int(self.plan.rank_offsets[-1].item())
@@ -171,8 +191,13 @@ class MoEBench:
         # fused tail: rows in, residual in, residual_out + norm_out, gamma, pos + weights
         tail_b = N * 2 * c.H + 3 * c.T * 2 * c.H + 2 * c.H + tk * 4 * 2
         addn_b = 4 * c.T * 2 * c.H + 2 * c.H                  # x, residual in; two rows out
+        # smoothed fp8 dispatch: x rows, the [E][H] fp32 scales once, codes +
+        # row scales out, ids + pos; fp8 combine: codes + row scales in, out rows
+        smooth_b = self.live_tokens * row_in + c.E * c.H * 4 + N * (c.H + 4) + tk * 4 * 2
+        combq_b = N * (c.H + 4) + c.T * 2 * c.H + tk * 4 * 2
         return {"ep_plan": plan_b, "ep_dispatch": disp_b, "ep_combine": comb_b,
-                "ep_combine_add_rmsnorm": tail_b, "ep_add_rmsnorm": addn_b}
+                "ep_combine_add_rmsnorm": tail_b, "ep_add_rmsnorm": addn_b,
+                "ep_dispatch_smooth": smooth_b, "ep_combine_quant": combq_b}
 
     def tokens(self):
         return self.cfg.T

@@ -151,6 +151,73 @@ __device__ __forceinline__ u32x4 quantize16f(const float* f, float scale) {
   return u32x4{out[0], out[1], out[2], out[3]};
 }
 
+// x / scale for one row's scale, correctly rounded, with the reciprocal
+// refined once per row.  The element step is the compiler's IEEE fp32
+// divide sequence without its operand scaling: q = n r, then two corrections
+// q += (n - s q) r by fused multiply-adds.  The scaling of that sequence only
+// acts on extreme exponents, so the fast form is taken for scales in
+// [2^-60, 2^60]; there every quotient of at least 2^-11 in magnitude has
+// normal operands and exact remainders, and smaller quotients (codes of
+// zero) keep the sign of n through the final copysign.  Other scales (zero,
+// subnormal, huge, infinite, NaN) take the plain division.
+struct RowDiv {
+  float s, r;
+  bool fast;
+};
+
+__device__ __forceinline__ RowDiv row_div(float scale) {
+  RowDiv d;
+  d.s = __int_as_float(uniform(__float_as_int(scale)));
+  d.fast = d.s >= 0x1p-60f && d.s <= 0x1p60f;
+  const float r0 = __builtin_amdgcn_rcpf(d.s);
+  d.r = __builtin_fmaf(__builtin_fmaf(-d.s, r0, 1.0f), r0, r0);
+  return d;
+}
+
+__device__ __forceinline__ float div_fast(float n, const RowDiv& d) {
+  float q = n * d.r;
+  float e = __builtin_fmaf(-d.s, q, n);
+  q = __builtin_fmaf(e, d.r, q);
+  e = __builtin_fmaf(-d.s, q, n);
+  q = __builtin_fmaf(e, d.r, q);
+  return __builtin_copysignf(q, n);
+}
+
+// Fast-path codes of 16 quotients.  fp8: gfx950's v_cvt_pk_fp8_f32 rounds
+// to nearest even into OCP E4M3FN and, after a clamp to +-448 (v_med3),
+// gives the code e4m3fn_code gives for every non-NaN input (all 2^32 fp32
+// patterns compared); the fast path never sees NaN.  int8: v_rndne, clamp,
+// convert.
+template <int QT>
+__device__ __forceinline__ u32x4 quantize16_fast(const float* f, const RowDiv& d) {
+  uint32_t out[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = div_fast(f[4 * i + j], d);
+    if constexpr (QT == kQFp8) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = __builtin_amdgcn_fmed3f(v[j], -448.0f, 448.0f);
+      int w = __builtin_amdgcn_cvt_pk_fp8_f32(v[0], v[1], 0, false);
+      w = __builtin_amdgcn_cvt_pk_fp8_f32(v[2], v[3], w, true);
+      out[i] = (uint32_t)w;
+    } else {
+      out[i] = int8_code(v[0]) | (int8_code(v[1]) << 8) | (int8_code(v[2]) << 16) | (int8_code(v[3]) << 24);
+    }
+  }
+  return u32x4{out[0], out[1], out[2], out[3]};
+}
+
+// Codes of 16 values of one row: the fast path, or the plain division and
+// the software encoders for rows whose scale is outside its range (a
+// row-uniform branch).
+template <int QT>
+__device__ __forceinline__ u32x4 quantize16r(const float* f, const RowDiv& d) {
+  if (d.fast) return quantize16_fast<QT>(f, d);
+  return quantize16f<QT>(f, d.s);
+}
+
 __device__ __forceinline__ void unpack16(const u32x4 a, const u32x4 b, float* f) {
   const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
@@ -162,10 +229,10 @@ __device__ __forceinline__ void unpack16(const u32x4 a, const u32x4 b, float* f)
 
 // Quantise 16 bf16 values (two 16-byte vectors) into 16 codes.
 template <int QT>
-__device__ __forceinline__ u32x4 quantize16(const u32x4 a, const u32x4 b, float scale) {
+__device__ __forceinline__ u32x4 quantize16(const u32x4 a, const u32x4 b, const RowDiv& d) {
   float f[16];
   unpack16(a, b, f);
-  return quantize16f<QT>(f, scale);
+  return quantize16r<QT>(f, d);
 }
 
 // Largest bf16 magnitude of two vectors, as the 15-bit magnitude pattern
@@ -221,12 +288,13 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_quant_kernel(
   for (int w = 1; w < kRowThreads / kWave; ++w) m = max(m, s_max[w]);
   const float amax = __uint_as_float(m << 16);
   const float scale = amax / quant_max<QT>();
+  const RowDiv rd = row_div(scale);
 
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int idx = g * kRowThreads + tid;
     if (idx < NG) {
-      const u32x4 code = quantize16<QT>(cache[g][0], cache[g][1], scale);
+      const u32x4 code = quantize16<QT>(cache[g][0], cache[g][1], rd);
       uint64_t mk = live;
       while (mk) {
         const int k = __builtin_ctzll(mk);
@@ -237,7 +305,7 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_quant_kernel(
     }
   }
   for (int idx = G * kRowThreads + tid; idx < NG; idx += kRowThreads) {
-    const u32x4 code = quantize16<QT>(ld<NTL>(src + 2 * idx), ld<NTL>(src + 2 * idx + 1), scale);
+    const u32x4 code = quantize16<QT>(ld<NTL>(src + 2 * idx), ld<NTL>(src + 2 * idx + 1), rd);
     uint64_t mk = live;
     while (mk) {
       const int k = __builtin_ctzll(mk);
@@ -397,10 +465,11 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_smooth_kernel(
 #pragma unroll
     for (int w = 1; w < kRowThreads / kWave; ++w) m = max(m, s_max[w]);
     const float scale = __uint_as_float(m) / quant_max<QT>();
+    const RowDiv rd = row_div(scale);
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       const int idx = g * kRowThreads + tid;
-      if (idx < NG) st<NTS>(q + (int64_t)p * NG + idx, quantize16f<QT>(xs[g], scale));
+      if (idx < NG) st<NTS>(q + (int64_t)p * NG + idx, quantize16r<QT>(xs[g], rd));
     }
     if (tid == 0) scales[p] = scale;
   }
@@ -412,16 +481,23 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_smooth_kernel(
 // weights as ep_combine does.  Work item: one wavefront per (token, chunk of
 // 1024 columns); a lane reads 16 codes (16 bytes) of each of the K rows.
 // ---------------------------------------------------------------------------
+// Four codes of one dword (byte i is code i) as fp32 values.  fp8:
+// v_cvt_pk_f32_fp8 decodes OCP E4M3FN codes exactly (all 256 codes compared
+// with the format's definition: sign, 4-bit exponent of bias 7, 3-bit
+// mantissa, subnormals below exponent 1; the two NaN codes give a NaN).
 template <int QT>
-__device__ __forceinline__ float decode_code(uint32_t c) {
-  if constexpr (QT == kQInt8) {
-    return (float)(int32_t)(int8_t)(c & 0xffu);
+__device__ __forceinline__ void decode4(uint32_t c, float* v) {
+  if constexpr (QT == kQFp8) {
+    typedef float f2 __attribute__((ext_vector_type(2)));
+    const f2 lo = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);
+    const f2 hi = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);
+    v[0] = lo.x;
+    v[1] = lo.y;
+    v[2] = hi.x;
+    v[3] = hi.y;
   } else {
-    const uint32_t sign = (c & 0x80u) << 24;
-    const uint32_t e = (c >> 3) & 15u, m = c & 7u;
-    if (e == 0) return __uint_as_float(sign | __float_as_uint((float)m * 0.001953125f));  // m * 2^-9
-    if (e == 15 && m == 7) return __uint_as_float(0x7fc00000u);
-    return __uint_as_float(sign | ((e + 120u) << 23) | (m << 20));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[j] = (float)(int32_t)(int8_t)((c >> (8 * j)) & 0xffu);
   }
 }
 
@@ -460,9 +536,11 @@ __global__ __launch_bounds__(kRowThreads) void combine_quant_kernel(
     if (pk[k] >= 0) {
       const uint32_t c4[4] = {r[k].x, r[k].y, r[k].z, r[k].w};
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float v = decode_code<QT>(c4[j / 4] >> (8 * (j % 4))) * sk[k];
-        acc[j] = __builtin_fmaf(wk[k], v, acc[j]);
+      for (int i = 0; i < 4; ++i) {
+        float v[4];
+        decode4<QT>(c4[i], v);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[4 * i + j] = __builtin_fmaf(wk[k], v[j] * sk[k], acc[4 * i + j]);
       }
     }
   }

@@ -181,3 +181,60 @@ def test_fullsize_smoothed_fp8_sampled():
     toks_t = torch.from_numpy(toks.astype(np.int64)).cuda()
     assert (bf16_ulp_distance(host(out[toks_t], np.uint16), want_out) == 0).all()
     assert ep.ep_device_error() == 0
+
+
+def e4m3_values():
+    """The 127 non-negative finite E4M3FN values, by code (format definition)."""
+    v = []
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        v.append(m * 2.0 ** -9 if e == 0 else (1 + m / 8) * 2.0 ** (e - 7))
+    return np.array(v)
+
+
+@pytest.mark.parametrize("qt", ["fp8", "int8"])
+def test_smoothed_codes_at_rounding_boundaries(qt):
+    """Quotients placed on and within three fp32 ulps of every rounding
+    boundary of the code (E4M3FN midpoints, int8 half-integers), both signs,
+    at many row scales (including scales outside [2^-60, 2^60] and
+    power-of-two ones).  x is all ones, so the smoothed row equals the
+    smoothing row, whose column 0 fixes the row maximum."""
+    print("quantisation at rounding boundaries", qt, flush=True)
+    dt, oq = QT[qt]
+    rng = np.random.default_rng(17 if qt == "fp8" else 18)
+    if qt == "fp8":
+        v = e4m3_values()
+        mids, qmax = (v[:-1] + v[1:]) / 2, np.float32(448.0)
+    else:
+        mids, qmax = np.arange(127) + 0.5, np.float32(127.0)
+    T, H = 96, 2048
+    E, K = T, 1
+    amax = (rng.uniform(0.5, 2.0, T) * 2.0 ** rng.integers(-40, 40, T)).astype(np.float32)
+    amax[:4] = np.float32([2.0 ** -70 * 1.37, 2.0 ** 70 * 1.61, 2.0 ** -64, 1.0])
+    amax[4:8] = np.float32(2.0) ** np.float32([-3, 0, 5, 17])
+    smooth = np.zeros((E, H), np.float32)
+    for t in range(T):
+        scale = np.float32(amax[t] / qmax)
+        cols = [amax[t]]
+        for m in mids:
+            base = np.float32(np.float32(m) * scale)
+            for k in range(-3, 4):
+                b = np.array([base], np.float32).view(np.uint32)[0]
+                nb = np.array([b + np.uint32(k) if k >= 0 else b - np.uint32(-k)], np.uint32)
+                val = nb.view(np.float32)[0]
+                if np.isfinite(val) and abs(val) <= amax[t]:
+                    cols += [val, -val]
+        cols = np.array(cols[:H], np.float32)
+        smooth[t, : cols.size] = cols
+        smooth[t, cols.size:] = rng.uniform(-1, 1, H - cols.size).astype(np.float32) * amax[t]
+    x = np.full((T, H), 0x3F80, np.uint16)                     # bf16 1.0
+    ids = np.arange(T, dtype=np.int32)[:, None]
+    p = oracle.plan(ids, E, 1)
+    q = torch.zeros((T, H), dtype=torch.uint8, device="cuda")
+    sc = torch.zeros((T,), dtype=torch.float32, device="cuda")
+    ep.ep_dispatch_smooth(dev(x), dev(ids), dev(p.pos), dev(smooth), q, sc, out_dtype=dt)
+    want_q, want_s = oracle.dispatch_quant(x, ids, p.pos, E, oq, T, smooth)
+    assert (host(sc).view(np.uint32) == want_s.view(np.uint32)).all()
+    bad = np.argwhere(host(q) != want_q)
+    assert bad.size == 0, f"{len(bad)} code mismatches, first at {bad[0].tolist()}"
+    assert ep.ep_device_error() == 0
