@@ -36,8 +36,13 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # the kernels built from the sources whose digest is `source_sha256`; any
 # other build reports traffic as null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": None,
-    "bytes_per_launch": {},   # {workload: {phase: bytes}}
+    "source_sha256": "42fa80dae2f486ac094d4979716e2f4ddb983f54f29385e0ee687fd9b2a18c4c",
+    "bytes_per_launch": {   # {workload: {phase: bytes}}
+        "2": {"ep_plan": 1938340, "ep_dispatch": 1059703497, "ep_combine": 1061203896, "ep_dispatch_smooth": 875791361, "ep_combine_quant": 600920270, "ep_combine_add_rmsnorm": 1294292406, "ep_add_rmsnorm": 470051162},
+        "4": {"ep_plan": 3586759, "ep_dispatch": 885934710, "ep_combine": 1652703342, "ep_dispatch_smooth": 2300551628, "ep_combine_quant": 969191959, "ep_combine_add_rmsnorm": 2118596952, "ep_add_rmsnorm": 939804411},
+        "1": {"ep_plan": 658629, "ep_dispatch": 235767403, "ep_combine": 236514597, "ep_dispatch_smooth": 144418591, "ep_combine_quant": 138683139},
+        "3": {"ep_plan_splits": 5120, "ep_dispatch_splits": 268542032},
+    },
 }
 
 
@@ -56,6 +61,20 @@ def measured_traffic(workload: int, phase: str):
     if TRAFFIC["source_sha256"] != source_digest():
         return None
     return TRAFFIC["bytes_per_launch"].get(str(workload), {}).get(phase)
+
+
+def host_cpu() -> dict:
+    """The host the CPU baseline ran on: model name and visible threads."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"host_cpu": model, "host_threads": os.cpu_count()}
 
 
 def log(*a):
@@ -202,6 +221,9 @@ class MoEBench:
     def tokens(self):
         return self.cfg.T
 
+    def live_tokens_count(self):
+        return self.live_tokens if self.inp.active is not None else None
+
     def config_record(self):
         c = self.cfg
         return {"workload": c.name + ("+add_rmsnorm_tail" if self.tail else ""),
@@ -289,6 +311,9 @@ class SplitsBench:
 
     def tokens(self):
         return self.cfg.W * self.cfg.R   # rows moved
+
+    def live_tokens_count(self):
+        return None
 
     def config_record(self):
         c = self.cfg
@@ -379,8 +404,25 @@ def main():
         b.record(stream)
         cold.append((a, b))
     torch.cuda.synchronize()
-    cold_ms = float(np.mean([a.elapsed_time(b) for a, b in cold]))
+    cold_list = [a.elapsed_time(b) for a, b in cold]
+    cold_ms = float(np.mean(cold_list))
     del scratch
+
+    # Warm steps, one event pair each, for the spread (the wall-clock figure
+    # above is the headline; these add the events' own cost per step).
+    warm = []
+    for _ in range(args.steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        step()
+        b.record(stream)
+        warm.append((a, b))
+    torch.cuda.synchronize()
+    warm_list = [a.elapsed_time(b) for a, b in warm]
+
+    def spread(ms):
+        return {f"p{q}": float(np.percentile(ms, q)) * 1e3 for q in (10, 50, 90)}
 
     # Per-launch durations: each phase launched `steps` times back to back
     # between two HIP events recorded on the launch stream; the average is
@@ -420,6 +462,8 @@ def main():
         "config": bench.config_record(),
         "hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "cold_ms_per_step": cold_ms,
+        "warm_step_us": spread(warm_list),
+        "cold_step_us": spread(cold_list),
         "cold_hbm_gbps": step_bytes / (cold_ms * 1e-3) / 1e9,
         "hbm_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
         "algorithmic_bytes_per_step": step_bytes,
@@ -427,15 +471,20 @@ def main():
         "source_sha256": source_digest(),
         "phase_us": {k: v * 1e3 for k, v in phase_ms.items()},
         "phase_gbps": {k: bpp[k] / (phase_ms[k] * 1e-3) / 1e9 for k in phase_ms},
+        "phase_algorithmic_bytes": {k: bpp[k] for k in phase_ms},
+        "phase_traffic_bytes": {k: measured_traffic(args.workload, k) for k in phase_ms},
         "step_phases": step_names,
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
                      "traffic": measured_traffic(args.workload, dominant),
                      "algorithmic_bytes_per_launch": bpp[dominant]},
     }
+    live = bench.live_tokens_count()
+    if live is not None:
+        rec["live_tokens_per_s"] = live / (ms_per_step * 1e-3)
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        rec["cpu_baseline"] = bench.cpu_baseline(args.cpu_reps)
+        rec["cpu_baseline"] = bench.cpu_baseline(args.cpu_reps) | host_cpu()
     print(json.dumps(rec), flush=True)
 
 
