@@ -157,9 +157,12 @@ __device__ __forceinline__ u32x4 quantize16f(const float* f, float scale) {
 // q += (n - s q) r by fused multiply-adds.  The scaling of that sequence only
 // acts on extreme exponents, so the fast form is taken for scales in
 // [2^-60, 2^60]; there every quotient of at least 2^-11 in magnitude has
-// normal operands and exact remainders, and smaller quotients (codes of
-// zero) keep the sign of n through the final copysign.  Other scales (zero,
-// subnormal, huge, infinite, NaN) take the plain division.
+// normal operands and exact remainders, and smaller quotients give codes of
+// zero.  The remainder is formed negated, e = s q - n, and subtracted,
+// q - e r: the same roundings (round to nearest is symmetric), and a zero n
+// keeps its sign through both corrections (with e = n - s q a -0 would come
+// back as +0).  Other scales (zero, subnormal, huge, infinite, NaN) take the
+// plain division.
 struct RowDiv {
   float s, r;
   bool fast;
@@ -176,11 +179,11 @@ __device__ __forceinline__ RowDiv row_div(float scale) {
 
 __device__ __forceinline__ float div_fast(float n, const RowDiv& d) {
   float q = n * d.r;
-  float e = __builtin_fmaf(-d.s, q, n);
-  q = __builtin_fmaf(e, d.r, q);
-  e = __builtin_fmaf(-d.s, q, n);
-  q = __builtin_fmaf(e, d.r, q);
-  return __builtin_copysignf(q, n);
+  float e = __builtin_fmaf(d.s, q, -n);
+  q = __builtin_fmaf(-e, d.r, q);
+  e = __builtin_fmaf(d.s, q, -n);
+  q = __builtin_fmaf(-e, d.r, q);
+  return q;
 }
 
 // Fast-path codes of 16 quotients.  fp8: gfx950's v_cvt_pk_fp8_f32 rounds
