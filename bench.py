@@ -37,12 +37,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # the kernels built from the sources whose digest is `source_sha256`; any
 # other build reports traffic as null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "42fa80dae2f486ac094d4979716e2f4ddb983f54f29385e0ee687fd9b2a18c4c",
+    "source_sha256": "a73c8752d67ee602c839e51baf0cf83d0ffedd73f958c19ef71e8ba8a1698e0d",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "2": {"ep_plan": 1938340, "ep_dispatch": 1059703497, "ep_combine": 1061203896, "ep_dispatch_smooth": 875791361, "ep_combine_quant": 600920270, "ep_combine_add_rmsnorm": 1294292406, "ep_add_rmsnorm": 470051162},
-        "4": {"ep_plan": 3586759, "ep_dispatch": 885934710, "ep_combine": 1652703342, "ep_dispatch_smooth": 2300551628, "ep_combine_quant": 969191959, "ep_combine_add_rmsnorm": 2118596952, "ep_add_rmsnorm": 939804411},
-        "1": {"ep_plan": 658629, "ep_dispatch": 235767403, "ep_combine": 236514597, "ep_dispatch_smooth": 144418591, "ep_combine_quant": 138683139},
-        "3": {"ep_plan_splits": 5120, "ep_dispatch_splits": 268542032},
+        "2": {"ep_plan": 1942761, "ep_dispatch": 1059692617, "ep_combine": 1061201273, "ep_dispatch_smooth": 875879688, "ep_combine_quant": 600906324, "ep_combine_add_rmsnorm": 1294289202, "ep_add_rmsnorm": 470047428},
+        "4": {"ep_plan": 3589674, "ep_dispatch": 885915394, "ep_combine": 1652699449, "ep_dispatch_smooth": 2300520205, "ep_combine_quant": 969231674, "ep_combine_add_rmsnorm": 2118593953, "ep_add_rmsnorm": 939802416},
+        "1": {"ep_plan": 661772, "ep_dispatch": 235744378, "ep_combine": 236513994, "ep_dispatch_smooth": 144420702, "ep_combine_quant": 138659618},
+        "3": {"ep_plan_splits": 5120, "ep_dispatch_splits": 268545551},
     },
 }
 
