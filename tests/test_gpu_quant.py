@@ -238,3 +238,27 @@ def test_smoothed_codes_at_rounding_boundaries(qt):
     bad = np.argwhere(host(q) != want_q)
     assert bad.size == 0, f"{len(bad)} code mismatches, first at {bad[0].tolist()}"
     assert ep.ep_device_error() == 0
+
+
+@pytest.mark.parametrize("qt", ["fp8", "int8"])
+def test_widest_rows(qt):
+    """H = 65536, the widest row the library takes: 16 groups of 16 values per
+    thread, 8 kept in registers and the rest re-read in the quantise pass;
+    then the combine of those rows."""
+    print("widest quantised rows", qt, flush=True)
+    dt, oq = QT[qt]
+    T, H, E, K, W = 12, 65536, 8, 3, 2
+    cfg, inp, p = case(T, H, E, K, W, 0.2, seed=65)
+    cap = cfg.cap_rows
+    q = torch.full((cap, H), 0x77, dtype=torch.uint8, device="cuda")
+    sc = torch.full((cap,), -5.0, dtype=torch.float32, device="cuda")
+    ep.ep_dispatch(dev(inp.x), dev(p.pos), q, sc, out_dtype=dt)
+    want_q, want_s = oracle.dispatch_quant(inp.x, inp.ids, p.pos, E, oq, cap, fill_q=0x77, fill_scale=-5.0)
+    assert (host(sc).view(np.uint32) == want_s.view(np.uint32)).all()
+    assert (host(q) == want_q).all()
+    out = torch.zeros((T, H), dtype=torch.int16, device="cuda")
+    ep.ep_combine_quant(q, sc, dev(p.pos), dev(inp.weights), out, code_dtype=dt)
+    want = oracle.combine_quant(want_q, oq, want_s, p.pos, inp.weights)
+    assert (bf16_ulp_distance(host(out, np.uint16), want) == 0).all()
+    assert (p.pos >= 0).any()
+    assert ep.ep_device_error() == 0
