@@ -110,21 +110,27 @@ __global__ __launch_bounds__(kPlanThreads) void plan_tile_kernel(
   const int cs = wave * seg;                       // wave's first copy, tile-relative
   const int ce = min(cs + seg, n);
 
-  // All of the wave's ids (and mask bytes) are requested before any is used.
+  // All of the wave's ids and mask bytes are requested before any is used
+  // (the bytes are combined once loaded: a short-circuit test would wait for
+  // each byte before issuing the next load).
   int e_reg[kPlanChunks];
-  bool act_reg[kPlanChunks];
+  uint32_t a_reg[kPlanChunks], ac_reg[kPlanChunks];
 #pragma unroll
   for (int ch = 0; ch < kPlanChunks; ++ch) {
     const int c = cs + ch * kWave + lane;
     e_reg[ch] = -1;
-    act_reg[ch] = false;
+    a_reg[ch] = 0;
+    ac_reg[ch] = 1;
     if (c < ce) {
       const int64_t gc = c0 + c;
       e_reg[ch] = ids[gc];
-      act_reg[ch] = (active == nullptr || active[gc / K] != 0) &&
-                    (active_copies == nullptr || active_copies[gc] != 0);
+      a_reg[ch] = active ? active[gc / K] : 1u;
+      if (active_copies) ac_reg[ch] = active_copies[gc];
     }
   }
+  bool act_reg[kPlanChunks];
+#pragma unroll
+  for (int ch = 0; ch < kPlanChunks; ++ch) act_reg[ch] = a_reg[ch] != 0 && ac_reg[ch] != 0;
 
   // Stable in-wave ranking, chunk by chunk, in flattened (t,k) order: peers
   // (lanes holding the same expert) come from one ballot per id bit; a lane's
@@ -496,21 +502,28 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
   const int cs = wave * seg;
   const int ce = min(cs + seg, n);
 
+  // All loads of the tile's ids and mask bytes go out together: the mask
+  // bytes are combined after the barrier (a short-circuit test here would
+  // wait for each byte before issuing the next load).
   int e_reg[kPlanChunks];
-  bool act_reg[kPlanChunks];
+  uint32_t a_reg[kPlanChunks], ac_reg[kPlanChunks];
 #pragma unroll
   for (int ch = 0; ch < kPlanChunks; ++ch) {
     const int c = cs + ch * kWave + lane;
     e_reg[ch] = -1;
-    act_reg[ch] = false;
+    a_reg[ch] = 0;
+    ac_reg[ch] = 1;
     if (c < ce) {
       const int64_t gc = c0 + c;
       e_reg[ch] = ids[gc];
-      act_reg[ch] = (active == nullptr || active[gc / K] != 0) &&
-                    (active_copies == nullptr || active_copies[gc] != 0);
+      a_reg[ch] = active ? active[gc / K] : 1u;
+      if (active_copies) ac_reg[ch] = active_copies[gc];
     }
   }
   __syncthreads();  // LDS zeroed
+  bool act_reg[kPlanChunks];
+#pragma unroll
+  for (int ch = 0; ch < kPlanChunks; ++ch) act_reg[ch] = a_reg[ch] != 0 && ac_reg[ch] != 0;
 
   int32_t* myhist = hist + wave * E;
   int r_reg[kPlanChunks];
@@ -603,16 +616,12 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
   }
   __syncthreads();
   // The last tile to finish reading advances the workspace's epoch; every
-  // tile read it at its start, before any tile could finish reading.
-  if (tid == 0) {
-    const uint32_t done =
-        __hip_atomic_fetch_add(&header[kHeaderDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == (uint32_t)ntiles - 1u) {
-      __hip_atomic_store(&header[kHeaderDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&header[kHeaderEpoch], epoch == 0xffffffffu ? 0u : epoch, __ATOMIC_RELAXED,
-                         __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+  // tile read it at its start, before any tile could finish reading.  The
+  // counter's old value is only looked at when the tile's work is done, so
+  // its round trip overlaps the rest of the kernel.
+  uint32_t done = 0;
+  if (tid == 0)
+    done = __hip_atomic_fetch_add(&header[kHeaderDone], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 
   // Final positions and occurrences of this tile's copies.
   int32_t* eoff = tot;  // padded, then scanned in place; true totals kept in cnt
@@ -657,6 +666,11 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
     __syncthreads();
     block_exclusive_scan_512(rin, E, wave_sums);
     for (int e = tid; e < E; e += kPlanThreads) src_offsets[(int64_t)g * E + e] = rin[e];
+  }
+  if (tid == 0 && done == (uint32_t)ntiles - 1u) {
+    __hip_atomic_store(&header[kHeaderDone], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(&header[kHeaderEpoch], epoch == 0xffffffffu ? 0u : epoch, __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
