@@ -7,8 +7,8 @@ through ctypes, taking and returning numpy arrays.  It shares no code with
 the HIP library and never imports it.
 
 Parity pins live in ``tests/test_oracle_*.py``.  Readings that nothing on the
-source pages pins (fp8 divide-by-scale, the all-zero token) are marked
-"parity unpinned" in ``ep_oracle.c``.
+source pages pins (quantisation divides by the scale; a row whose amax is 0
+gets scale 0 and zero codes) are marked "parity unpinned" in ``ep_oracle.c``.
 """
 from __future__ import annotations
 

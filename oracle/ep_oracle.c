@@ -33,8 +33,9 @@
  * Parity pins: every function is pinned by the -m "not gpu" tests (worked
  * examples from [P1] and [P3], brute force, closed forms, library
  * cross-checks).  The two readings that nothing on the pages can pin are
- * marked "parity unpinned" where they occur (fp8: divide-by-scale and the
- * all-zero token).
+ * marked "parity unpinned" where they occur: quantisation (fp8 or int8,
+ * with or without smoothing) divides by the scale, and a row whose amax is
+ * 0 gets scale 0 and zero codes.
  */
 #include <math.h>
 #include <stdint.h>
@@ -573,7 +574,9 @@ static double orc_decode(int qtype, uint8_t code)
  *   q[h]   = code(fl32(xs[h] / scale))  (E4M3FN RNE saturating, or int8 RNE
  *            clamped to +-127), all codes 0 when scale == 0
  *   expand_q[pos] = q, expand_scales[pos] = scale.
- * Without smoothing every copy of a token carries the same row. */
+ * Without smoothing every copy of a token carries the same row.
+ * Readings (parity unpinned, as for the fp8 dispatch above): one IEEE
+ * division by the scale, and zero codes for a row whose amax is 0. */
 int oracle_dispatch_quant(int32_t T, int32_t K, int32_t E, int32_t H, const uint16_t *x,
                           const int32_t *ids, const int32_t *pos, const float *smooth,
                           int32_t qtype, uint8_t *expand_q, float *expand_scales,
