@@ -66,8 +66,8 @@ typedef enum {
 
 /* Limits: 1 <= K <= 16 and 1 <= E <= 1024 (the dispatch page's top-K and
  * expert-count limits), W >= 1, W divides E and T, T * K < 2^31,
- * H % 8 == 0 for bf16 rows and H % 16 == 0 for fp8 rows (16-byte vectors),
- * H <= 65536. */
+ * H % 8 == 0 for bf16 rows and H % 16 == 0 for fp8 and int8 rows (16-byte
+ * vectors), H <= 65536. */
 #define EP_MAX_K 16
 #define EP_MAX_E 1024
 #define EP_MAX_H 65536
@@ -181,9 +181,13 @@ int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t *topk_ids,
  *                  expand_x[pos][h] = E4M3FN_rne_sat(fl32(x[t][h] / scale))
  *                  (all codes 0x00 when scale == 0), expand_scales[pos] = scale
  *                  (dynamicScalesOut: one fp32 scale per expanded row).
+ *   EP_INT8:       the same with scale = fl32(amax / 127) and int8 codes:
+ *                  the nearest integer of fl32(x[t][h] / scale), ties to even,
+ *                  clamped to [-127, 127] (INT8 is the output type of
+ *                  quantMode 2 on the CANN page).
  * x [T][H] bf16; expand_x [cap_rows][H] (uint16 bf16, or uint8 codes; H % 16
  * for codes);
- * expand_scales [cap_rows] fp32, required for fp8, ignored for bf16.
+ * expand_scales [cap_rows] fp32, required for fp8 and int8, ignored for bf16.
  * weights [T][K] fp32 and expand_weights [cap_rows] fp32, both or neither:
  * expand_weights[pos[t][k]] = weights[t][k], the gate weight carried to each
  * expanded row (expandScalesOut on the CANN dispatch page).
@@ -228,7 +232,8 @@ int ep_dispatch_smooth(int32_t T, int32_t K, int32_t E, int32_t H, const uint16_
  *   out[t][h] = bf16_rne(sum over live k of w[t][k] * y[pos[t][k]][h]),
  * fp32 fused multiply-adds in increasing k from +0, as ep_combine.
  * codes [cap_rows][H] uint8 (E4M3FN or int8 per code_dtype), row_scales
- * [cap_rows] fp32, out [T][H] bf16; H % 16 == 0. */
+ * [cap_rows] fp32, weights [T][K] fp32, out [T][H] bf16; H % 16 == 0;
+ * codes and out 16-byte aligned; every pos must be < cap_rows. */
 int ep_combine_quant(int32_t T, int32_t K, int32_t H, const void *codes, int32_t code_dtype,
                      const float *row_scales, int64_t cap_rows, const int32_t *pos,
                      const float *weights, uint16_t *out, void *stream);
