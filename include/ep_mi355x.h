@@ -59,8 +59,10 @@ typedef enum {
 /* Device error bits (ep_device_error). */
 #define EP_DEVERR_BAD_EXPERT 1 /* a live copy named an expert outside [0,E) */
 #define EP_DEVERR_SPLITS 2     /* a 1-D plan named rows outside the buffers */
-#define EP_DEVERR_PLAN_STALL 4 /* the plan's look-back waited too long (the
-                                  workspace was not initialised): plan invalid */
+#define EP_DEVERR_PLAN_STALL 4 /* a wait of the plan hit its spin limit (the
+                                  workspace was not initialised, or another
+                                  stream's kernel held the compute units for
+                                  about a second): plan invalid */
 #define EP_DEVERR_BAD_ROW 8    /* dispatch/combine met a pos >= cap_rows: that
                                   copy was skipped */
 
@@ -169,7 +171,12 @@ int ep_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  * The result is deterministic and identical to the serial definition.
  * T == 0 writes the all-zero plan.  The workspace (size from
  * ep_workspace_size, initialised once with ep_workspace_init) must not be
- * used by two calls in flight at the same time. */
+ * used by two calls in flight at the same time.
+ * When all of its tiles fit on the device at once the plan is one launch
+ * whose tiles exchange counts while running; every wait is bounded, so a
+ * kernel on another stream that keeps the compute units busy for about a
+ * second makes the plan give up with EP_DEVERR_PLAN_STALL rather than hang.
+ * Larger grids use a look-back that only waits on tiles already running. */
 int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t *topk_ids,
             const uint8_t *active, const ep_plan_opts_t *opts, const ep_plan_t *plan,
             void *workspace, size_t ws_bytes, void *stream);
