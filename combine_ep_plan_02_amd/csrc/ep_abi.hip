@@ -34,7 +34,7 @@
 // to streaming stores.
 constexpr bool kDispatchNtLoad = false, kDispatchNtStore = true;
 constexpr bool kCombineNtLoad = true, kCombineNtStore = true;
-constexpr bool kFp8NtLoad = false, kFp8NtStore = true;
+constexpr bool kQuantNtLoad = false, kQuantNtStore = true;
 constexpr bool kCopyNtLoad = false, kCopyNtStore = true;
 // Vectors per lane of one (token, column chunk) work item.
 constexpr int kDispatchUnroll = 2;
@@ -319,34 +319,34 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
                 (long long)T * K);
   if (T == 0) return ok();
   if (!x || !pos || !expand_x) return fail(EP_ERR_NULLPTR, "x, pos and expand_x are required");
-  const bool fp8 = out_dtype != EP_BF16;  // quantised rows: fp8 or int8 codes + scales
-  if (fp8 && !expand_scales) return fail(EP_ERR_NULLPTR, "expand_scales is required for quantised rows");
+  const bool quant = out_dtype != EP_BF16;  // fp8 or int8 codes + one scale per row
+  if (quant && !expand_scales) return fail(EP_ERR_NULLPTR, "expand_scales is required for quantised rows");
   if (!aligned(x, 16) || !aligned(expand_x, 16))
     return fail(EP_ERR_INVALID, "x and expand_x must be 16-byte aligned");
-  if (!aligned(pos, 4) || (fp8 && !aligned(expand_scales, 4)))
+  if (!aligned(pos, 4) || (quant && !aligned(expand_scales, 4)))
     return fail(EP_ERR_INVALID, "pos and expand_scales must be 4-byte aligned");
   if ((weights == nullptr) != (expand_weights == nullptr))
     return fail(EP_ERR_NULLPTR, "weights and expand_weights go together");
   if (!aligned(weights, 4) || !aligned(expand_weights, 4))
     return fail(EP_ERR_INVALID, "weights and expand_weights must be 4-byte aligned");
   const size_t xb = (size_t)T * H * 2, pb = (size_t)T * K * 4;
-  const size_t eb = (size_t)cap_rows * H * (fp8 ? 1 : 2);
-  const size_t sb = fp8 ? (size_t)cap_rows * 4 : 0;
+  const size_t eb = (size_t)cap_rows * H * (quant ? 1 : 2);
+  const size_t sb = quant ? (size_t)cap_rows * 4 : 0;
   if (overlap(expand_x, eb, x, xb) || overlap(expand_x, eb, pos, pb))
     return fail(EP_ERR_INVALID, "expand_x overlaps an input");
-  if (fp8 && (overlap(expand_scales, sb, x, xb) || overlap(expand_scales, sb, pos, pb) ||
+  if (quant && (overlap(expand_scales, sb, x, xb) || overlap(expand_scales, sb, pos, pb) ||
               overlap(expand_scales, sb, expand_x, eb)))
     return fail(EP_ERR_INVALID, "expand_scales overlaps another buffer");
   const size_t wb = expand_weights ? (size_t)cap_rows * 4 : 0;
   if (expand_weights &&
       (overlap(expand_weights, wb, x, xb) || overlap(expand_weights, wb, pos, pb) ||
        overlap(expand_weights, wb, expand_x, eb) || overlap(expand_weights, wb, weights, pb) ||
-       (fp8 && overlap(expand_weights, wb, expand_scales, sb))))
+       (quant && overlap(expand_weights, wb, expand_scales, sb))))
     return fail(EP_ERR_INVALID, "expand_weights overlaps another buffer");
 
   hipStream_t s = (hipStream_t)stream;
   const dim3 block(ep::kRowThreads);
-  if (!fp8) {
+  if (!quant) {
     const int V = H / 8;
     const int chunks = (V + ep::kWave * kDispatchUnroll - 1) / (ep::kWave * kDispatchUnroll);
     const int64_t items = (int64_t)T * chunks;
@@ -366,7 +366,7 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
   auto launch = [&](auto qt) {
     constexpr int QT = decltype(qt)::value;
 #define EP_QDISP(G)                                                                                          \
-  hipLaunchKernelGGL((ep::dispatch_quant_kernel<QT, G, kFp8NtLoad, kFp8NtStore>), tgrid, block, 0, s, xv, pos, qv, \
+  hipLaunchKernelGGL((ep::dispatch_quant_kernel<QT, G, kQuantNtLoad, kQuantNtStore>), tgrid, block, 0, s, xv, pos, qv, \
                      expand_scales, weights, expand_weights, T, K, NG, cap_rows)
     if (per_thread <= 1) EP_QDISP(1);
     else if (per_thread <= 2) EP_QDISP(2);
@@ -458,7 +458,7 @@ EP_EXPORT int ep_dispatch_smooth(int32_t T, int32_t K, int32_t E, int32_t H, con
   auto launch = [&](auto qt) {
     constexpr int QT = decltype(qt)::value;
 #define EP_SMOOTH(G)                                                                                      \
-  hipLaunchKernelGGL((ep::dispatch_smooth_kernel<QT, G, kFp8NtStore>), dim3((unsigned)T), dim3(ep::kRowThreads), \
+  hipLaunchKernelGGL((ep::dispatch_smooth_kernel<QT, G, kQuantNtStore>), dim3((unsigned)T), dim3(ep::kRowThreads), \
                      0, s, xv, topk_ids, pos, sm, qv, expand_scales, T, K, E, NG, cap_rows)
     if (per_thread <= 1) EP_SMOOTH(1);
     else if (per_thread <= 2) EP_SMOOTH(2);

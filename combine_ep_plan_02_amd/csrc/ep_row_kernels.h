@@ -1,11 +1,13 @@
-// ep_row_kernels.h -- HBM-bound row movers: dispatch scatter (bf16 and
-// per-token dynamic fp8), weighted combine gather, and the 1-D uneven
-// all-to-all (plan + chunk copy).
+// ep_row_kernels.h -- the row kernels: dispatch scatter (bf16 rows, or per-token
+// dynamic fp8 / int8 codes, optionally after per-expert smoothing), the
+// weighted combine gather (of bf16 or quantised rows, optionally fused with
+// the residual add and RMSNorm), and the 1-D uneven all-to-all (plan + chunk
+// copy).
 //
-// Token-major, one wavefront per token: a token's positions (K <= 16) are read
-// once by the first K lanes and broadcast with v_readlane, so the row loop
-// carries no per-element index math; every row moves as 16-byte vectors, 64
-// lanes side by side (1 KiB per wave instruction), fully coalesced.
+// Token-major: a token's positions (K <= 16) are read once by the first K
+// lanes of a wavefront and broadcast with v_readlane, so the row loops carry
+// no per-element index math; every row moves as 16-byte vectors, 64 lanes
+// side by side (1 KiB per wave instruction), fully coalesced.
 #pragma once
 
 #include "ep_common.h"
@@ -87,10 +89,12 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// Dispatch with per-token dynamic quantisation to OCP fp8 E4M3FN (quantMode 2
-// of the CANN "aclnnMoeDistributeDispatchV2" page; one fp32 scale per
-// expanded row, as dynamicScalesOut):
-//   scale = fl32(amax / 448),  code = E4M3FN_rne_sat(fl32(x / scale)).
+// Dispatch with per-token dynamic quantisation (quantMode 2 of the CANN
+// "aclnnMoeDistributeDispatchV2" page; one fp32 scale per expanded row, as
+// dynamicScalesOut), to OCP fp8 E4M3FN or int8:
+//   scale = fl32(amax / qmax),  code = encode(fl32(x / scale)),
+// qmax = 448 (E4M3FN, round to nearest even, saturating) or 127 (int8,
+// nearest integer, ties to even, clamped).
 // ---------------------------------------------------------------------------
 
 // fp32 -> E4M3FN, round to nearest even, saturating to +-448; NaN -> 0x7f.
