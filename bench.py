@@ -37,12 +37,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # the kernels built from the sources whose digest is `source_sha256`; any
 # other build reports traffic as null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "a73c8752d67ee602c839e51baf0cf83d0ffedd73f958c19ef71e8ba8a1698e0d",
+    "source_sha256": "1db59e6f40bb4ea93c2c8994aaa36054c9b4dc11f026ffd1e50efb7ce6757623",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "2": {"ep_plan": 1942761, "ep_dispatch": 1059692617, "ep_combine": 1061201273, "ep_dispatch_smooth": 875879688, "ep_combine_quant": 600906324, "ep_combine_add_rmsnorm": 1294289202, "ep_add_rmsnorm": 470047428},
-        "4": {"ep_plan": 3589674, "ep_dispatch": 885915394, "ep_combine": 1652699449, "ep_dispatch_smooth": 2300520205, "ep_combine_quant": 969231674, "ep_combine_add_rmsnorm": 2118593953, "ep_add_rmsnorm": 939802416},
-        "1": {"ep_plan": 661772, "ep_dispatch": 235744378, "ep_combine": 236513994, "ep_dispatch_smooth": 144420702, "ep_combine_quant": 138659618},
-        "3": {"ep_plan_splits": 5120, "ep_dispatch_splits": 268545551},
+        "2": {"ep_plan": 1938425, "ep_dispatch": 1059659374, "ep_combine": 1061186748, "ep_dispatch_smooth": 875929187, "ep_combine_quant": 600525509, "ep_combine_add_rmsnorm": 1294293065, "ep_add_rmsnorm": 470058844},
+        "4": {"ep_plan": 3561170, "ep_dispatch": 885904546, "ep_combine": 1652684813, "ep_dispatch_smooth": 2301777536, "ep_combine_quant": 969457219, "ep_combine_add_rmsnorm": 2118578239, "ep_add_rmsnorm": 939813633},
+        "1": {"ep_plan": 652724, "ep_dispatch": 235760941, "ep_combine": 236502921, "ep_dispatch_smooth": 144420743, "ep_combine_quant": 138612913},
+        "3": {"ep_plan_splits": 6144, "ep_dispatch_splits": 268555528},
     },
 }
 
