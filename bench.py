@@ -87,8 +87,12 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4],
-                    help="index of the workload (2: T=8192 H=7168 E=256 K=8 W=16 Zipf)")
+    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4],
+                    help="index of the workload (2: T=8192 H=7168 E=256 K=8 W=16 Zipf; "
+                         "0: the T=64 latency case)")
+    ap.add_argument("--graph", action="store_true",
+                    help="capture one step into a HIP graph and time its replays (no host "
+                         "launch cost per kernel; what a launch-bound small step needs)")
     ap.add_argument("--tail", action="store_true",
                     help="end the step with the fused combine + residual add + RMSNorm tail "
                          "(ep_combine_add_rmsnorm) instead of ep_combine; the unfused pair "
@@ -383,6 +387,19 @@ def main():
         step()
     torch.cuda.synchronize()
     assert ep.ep_device_error() == 0
+    eager_step = step
+    if args.graph:
+        # The library enqueues kernels only (no allocation, memset or host
+        # read-back), so the whole step is captured once and replayed.
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            eager_step()
+        torch.cuda.synchronize()
+        step = graph.replay
+        for _ in range(max(1, args.warmup)):
+            step()
+        torch.cuda.synchronize()
+        assert ep.ep_device_error() == 0
 
     # Timed region: exactly `steps` steps, synchronised on both sides.
     log(f"[bench] timing {args.steps} steps")
@@ -446,7 +463,7 @@ def main():
         b.record(stream)
         torch.cuda.synchronize()
         phase_ms[name] = a.elapsed_time(b) / args.steps
-    step()  # leave the buffers in the state of one whole step
+    eager_step()  # leave the buffers in the state of one whole step
     torch.cuda.synchronize()
     assert ep.ep_device_error() == 0
 
@@ -465,7 +482,7 @@ def main():
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
         "dtype": bench.dtype(), "data": "synthetic (seeded numpy generators, see workloads.py)",
-        "config": bench.config_record(),
+        "config": bench.config_record() | ({"launch": "hip_graph_replay"} if args.graph else {}),
         "hbm_gbps": step_bytes / (ms_per_step * 1e-3) / 1e9,
         "cold_ms_per_step": cold_ms,
         "warm_step_us": spread(warm_list),
