@@ -353,7 +353,7 @@ class SplitsBench:
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print(json.dumps({"error": "this build runs on one GPU only: the W expert-parallel "
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the W expert-parallel "
                           "ranks are emulated as buffers in one GPU's HBM; run with --gpus 1"}),
               flush=True)
         sys.exit(2)
@@ -370,7 +370,7 @@ def main():
     import combine_ep_plan_02_amd as ep
     import workloads
 
-    cfg = workloads.CONFIGS[args.workload]
+    cfg = workloads.WORKLOADS[args.workload]
     if args.workload == 3:
         bench = SplitsBench(cfg, torch, ep, workloads)
     else:

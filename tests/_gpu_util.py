@@ -39,7 +39,7 @@ def bf16_ulp_distance(a: np.ndarray, b: np.ndarray) -> np.ndarray:
     return np.abs(ordered(a) - ordered(b))
 
 
-class GpuRun:
+class GpuPath:
     """Plan + dispatch + combine of one input set on the GPU."""
 
     def __init__(self, ids, E, W, active=None, with_occ=True):

@@ -15,7 +15,7 @@ import torch
 import combine_ep_plan_02_amd as ep
 import oracle
 import workloads
-from _gpu_util import GpuRun, assert_plan_equal, bf16_ulp_distance, dev, host
+from _gpu_util import GpuPath, assert_plan_equal, bf16_ulp_distance, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -43,14 +43,14 @@ def sub_problem(pos, tokens):
 
 @pytest.mark.parametrize("idx", [1, 2, 4])
 def test_fullsize_workload(idx):
-    cfg = workloads.CONFIGS[idx]
+    cfg = workloads.WORKLOADS[idx]
     say("full-size workload", idx, cfg.name)
     ep.ep_device_error()
     inp = workloads.moe_inputs(cfg)
     want = oracle.plan(inp.ids, cfg.E, cfg.W, inp.active)
     N = want.n_rows
     cap = cfg.cap_rows
-    g = GpuRun(inp.ids, cfg.E, cfg.W, inp.active)
+    g = GpuPath(inp.ids, cfg.E, cfg.W, inp.active)
     g.run_plan()
     assert_plan_equal(g.plan_host(), want)
     say("  plan ok, N =", N)

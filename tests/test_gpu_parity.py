@@ -13,7 +13,7 @@ import torch
 import combine_ep_plan_02_amd as ep
 import oracle
 import workloads
-from _gpu_util import GpuRun, assert_plan_equal, bf16_ulp_distance, dev, host
+from _gpu_util import GpuPath, assert_plan_equal, bf16_ulp_distance, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -65,7 +65,7 @@ def test_plan_parity(case):
     say("plan case", case)
     ids, active = random_case(T, K, E, W, mask, seed, routing)
     want = oracle.plan(ids, E, W, active)
-    g = GpuRun(ids, E, W, active)
+    g = GpuPath(ids, E, W, active)
     g.run_plan()
     assert_plan_equal(g.plan_host(), want)
     assert ep.ep_device_error() == 0
@@ -74,7 +74,7 @@ def test_plan_parity(case):
 def test_plan_empty_tokens():
     say("plan T=0")
     ids = np.zeros((0, 4), np.int32)
-    g = GpuRun(ids, 8, 2)
+    g = GpuPath(ids, 8, 2)
     for f in ("in_splits", "expert_counts", "rank_offsets"):
         getattr(g.plan, f).fill_(-7)
     g.run_plan()
@@ -93,7 +93,7 @@ def test_plan_invalid_ids_are_dropped_and_flagged():
     active = np.ones(T, np.uint8)
     active[200] = 0          # an inactive token's bad id is not an error by itself
     want = oracle.plan(ids, E, W, active)
-    g = GpuRun(ids, E, W, active)
+    g = GpuPath(ids, E, W, active)
     g.run_plan()
     assert_plan_equal(g.plan_host(), want)
     assert ep.ep_device_error() == ep.EP_DEVERR_BAD_EXPERT == want.err
@@ -102,7 +102,7 @@ def test_plan_invalid_ids_are_dropped_and_flagged():
 def test_plan_reuse_and_determinism():
     say("plan reuse")
     ids, active = random_case(3000, 5, 60, 6, 0.3, 1)
-    g = GpuRun(ids, 60, 6, active)
+    g = GpuPath(ids, 60, 6, active)
     first = None
     for _ in range(3):  # the workspace is left ready for the next call
         g.run_plan()
@@ -122,7 +122,7 @@ def test_dispatch_bf16_and_combine_parity(H):
     inp = workloads.moe_inputs(cfg)
     p = oracle.plan(inp.ids, E, W, inp.active)
     cap = cfg.cap_rows
-    g = GpuRun(inp.ids, E, W, inp.active)
+    g = GpuPath(inp.ids, E, W, inp.active)
     g.run_plan()
     x = dev(inp.x)
     ex = torch.full((cap, H), 0x5A5A, dtype=torch.int16, device="cuda")  # sentinel rows
@@ -148,7 +148,7 @@ def test_combine_parity_random_rows(K):
     p = oracle.plan(inp.ids, E, W, inp.active)
     y = workloads.expert_outputs(cfg.cap_rows, H, seed=K)
     w = inp.weights * np.float32(1.7)
-    g = GpuRun(inp.ids, E, W, inp.active)
+    g = GpuPath(inp.ids, E, W, inp.active)
     g.run_plan()
     out = torch.empty((T, H), dtype=torch.int16, device="cuda")
     ep.ep_combine(dev(y), g.plan.pos, dev(w), out)
@@ -164,7 +164,7 @@ def test_combine_closed_forms():
     T, H, E, W, K = 64, 256, 8, 2, 6
     cfg = workloads.MoEConfig("t", T=T, H=H, E=E, K=K, W=W, mask_frac=0.25, seed=3)
     inp = workloads.moe_inputs(cfg)
-    g = GpuRun(inp.ids, E, W, inp.active)
+    g = GpuPath(inp.ids, E, W, inp.active)
     g.run_plan()
     ex = torch.zeros((cfg.cap_rows, H), dtype=torch.int16, device="cuda")
     ep.ep_dispatch(dev(inp.x), g.plan.pos, ex)
@@ -204,7 +204,7 @@ def test_dispatch_fp8_parity(H):
     p = oracle.plan(inp.ids, E, W, act)
     cap = cfg.cap_rows
     want_q, want_s = oracle.dispatch_fp8(x, p.pos, cap, fill_q=0xA5, fill_scale=-2.0)
-    g = GpuRun(inp.ids, E, W, act)
+    g = GpuPath(inp.ids, E, W, act)
     g.run_plan()
     q = torch.full((cap, H), 0xA5, dtype=torch.uint8, device="cuda")
     sc = torch.full((cap,), -2.0, dtype=torch.float32, device="cuda")
@@ -305,7 +305,7 @@ def test_splits_bad_plan_is_flagged():
 
 
 def test_splits_config3_full():
-    cfg = workloads.CONFIGS[3]
+    cfg = workloads.WORKLOADS[3]
     say("splits config 3 full", cfg)
     send, inp = workloads.splits_inputs(cfg)
     sp, out = run_splits(send, inp)

@@ -153,7 +153,7 @@ def test_fullsize_smoothed_fp8_sampled():
     """The largest workload (T16384 H7168 E256 K8, 25% masked tokens) through
     the smoothed fp8 dispatch and the quantised combine, compared on a sample
     of tokens with the oracle."""
-    cfg = workloads.CONFIGS[4]
+    cfg = workloads.WORKLOADS[4]
     print("full-size smoothed fp8", cfg.name, flush=True)
     inp = workloads.moe_inputs(cfg)
     p = oracle.plan(inp.ids, cfg.E, cfg.W, inp.active)

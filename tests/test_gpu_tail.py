@@ -10,7 +10,7 @@ import torch
 import combine_ep_plan_02_amd as ep
 import oracle
 import workloads
-from _gpu_util import GpuRun, bf16_ulp_distance, dev, host
+from _gpu_util import GpuPath, bf16_ulp_distance, dev, host
 
 pytestmark = pytest.mark.gpu
 
@@ -32,7 +32,7 @@ def test_tail_parity(H, K):
     cfg, inp, y, residual, gamma = tail_inputs(T, H, E, K, W, H + K)
     p = oracle.plan(inp.ids, E, W, inp.active)
     want_ro, want_no = oracle.combine_add_rmsnorm(y, p.pos, inp.weights, residual, gamma, eps)
-    g = GpuRun(inp.ids, E, W, inp.active)
+    g = GpuPath(inp.ids, E, W, inp.active)
     g.run_plan()
     ro = torch.empty((T, H), dtype=torch.int16, device="cuda")
     no = torch.empty((T, H), dtype=torch.int16, device="cuda")
@@ -68,11 +68,11 @@ def test_tail_alone_parity():
 
 
 def test_tail_fullsize_sampled():
-    cfg = workloads.CONFIGS[2]
+    cfg = workloads.WORKLOADS[2]
     print("tail full size", cfg.name, flush=True)
     inp = workloads.moe_inputs(cfg)
     want = oracle.plan(inp.ids, cfg.E, cfg.W, inp.active)
-    g = GpuRun(inp.ids, cfg.E, cfg.W, inp.active)
+    g = GpuPath(inp.ids, cfg.E, cfg.W, inp.active)
     g.run_plan()
     ex = torch.empty((cfg.cap_rows, cfg.H), dtype=torch.int16, device="cuda")
     ep.ep_dispatch(dev(inp.x), g.plan.pos, ex)

@@ -114,7 +114,7 @@ def test_random_matches_padded_even(seed):
 
 
 def test_config3_send_matrix():
-    cfg = workloads.CONFIGS[3]
+    cfg = workloads.WORKLOADS[3]
     send = workloads.send_matrix(cfg)
     assert (send.sum(axis=1) == cfg.R).all()
     assert not (send == send.T).all()

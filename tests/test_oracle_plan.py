@@ -126,7 +126,7 @@ def check_plan_invariants(p, ids, E, W, active):
 
 @pytest.mark.parametrize("cfg_idx", [0])
 def test_plan_invariants_config0(cfg_idx):
-    cfg = workloads.CONFIGS[cfg_idx]
+    cfg = workloads.WORKLOADS[cfg_idx]
     inp = workloads.moe_inputs(cfg, with_x=False)
     p = oracle.plan(inp.ids, cfg.E, cfg.W, inp.active)
     check_plan_invariants(p, inp.ids, cfg.E, cfg.W, inp.active)
@@ -169,7 +169,7 @@ def test_dst_offsets_match_destination_view():
 
 
 def test_zipf_config_has_empty_experts():
-    cfg = workloads.CONFIGS[2]
+    cfg = workloads.WORKLOADS[2]
     inp = workloads.moe_inputs(cfg, with_x=False)
     p = oracle.plan(inp.ids, cfg.E, cfg.W, inp.active)
     assert int((p.expert_counts == 0).sum()) >= cfg.n_empty

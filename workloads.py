@@ -63,7 +63,7 @@ class SplitsConfig:
 
 
 # The five workloads of the benchmark suite.
-CONFIGS = {
+WORKLOADS = {
     0: MoEConfig("tiny_T64_H128_E8_K2_W2", T=64, H=128, E=8, K=2, W=2, seed=0),
     1: MoEConfig("T4096_H4096_E64_K6_W8", T=4096, H=4096, E=64, K=6, W=8, seed=1),
     2: MoEConfig("T8192_H7168_E256_K8_W16_zipf1.2", T=8192, H=7168, E=256, K=8, W=16,
