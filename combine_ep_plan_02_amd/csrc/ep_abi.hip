@@ -39,6 +39,12 @@ constexpr bool kCopyNtLoad = false, kCopyNtStore = true;
 // Vectors per lane of one (token, column chunk) work item.
 constexpr int kDispatchUnroll = 2;
 constexpr int kCombineUnroll = 1;
+// Waves (work items) per workgroup of the combine gathers.  bf16 rows: 2
+// measured ~3% faster than 4 or 8 at T=8192, H=7168, K=8 (1 and 16 in
+// between).  Code rows: 4 (2 was no faster at H=7168 and 3% slower at
+// T=4096, H=4096).
+constexpr int kCombineWaves = 2;
+constexpr int kCombineQuantWaves = 4;
 
 namespace {
 
@@ -397,24 +403,24 @@ EP_EXPORT int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t* y, int
     return fail(EP_ERR_INVALID, "out overlaps an input");
 
   hipStream_t s = (hipStream_t)stream;
-  const dim3 block(ep::kRowThreads);
+  const dim3 block(kCombineWaves * ep::kWave);
   const int V = H / 8;
   const int chunks = (V + ep::kWave * kCombineUnroll - 1) / (ep::kWave * kCombineUnroll);
   const int64_t items = (int64_t)T * chunks;
-  if ((items + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock > INT32_MAX)
+  if ((items + kCombineWaves - 1) / kCombineWaves > INT32_MAX)
     return fail(EP_ERR_UNSUPPORTED, "T * H too large for one launch");
-  const dim3 cgrid((unsigned)((items + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock));
+  const dim3 cgrid((unsigned)((items + kCombineWaves - 1) / kCombineWaves));
   const ep::u32x4* yv = (const ep::u32x4*)y;
   ep::u32x4* ov = (ep::u32x4*)out;
   if (K <= 4)
-    hipLaunchKernelGGL((ep::combine_kernel<4, kCombineUnroll, kCombineNtLoad, kCombineNtStore>), cgrid, block, 0,
-                       s, yv, pos, weights, ov, T, K, V, chunks, cap_rows);
+    hipLaunchKernelGGL((ep::combine_kernel<4, kCombineUnroll, kCombineWaves, kCombineNtLoad, kCombineNtStore>),
+                       cgrid, block, 0, s, yv, pos, weights, ov, T, K, V, chunks, cap_rows);
   else if (K <= 8)
-    hipLaunchKernelGGL((ep::combine_kernel<8, kCombineUnroll, kCombineNtLoad, kCombineNtStore>), cgrid, block, 0,
-                       s, yv, pos, weights, ov, T, K, V, chunks, cap_rows);
+    hipLaunchKernelGGL((ep::combine_kernel<8, kCombineUnroll, kCombineWaves, kCombineNtLoad, kCombineNtStore>),
+                       cgrid, block, 0, s, yv, pos, weights, ov, T, K, V, chunks, cap_rows);
   else
-    hipLaunchKernelGGL((ep::combine_kernel<16, kCombineUnroll, kCombineNtLoad, kCombineNtStore>), cgrid, block, 0,
-                       s, yv, pos, weights, ov, T, K, V, chunks, cap_rows);
+    hipLaunchKernelGGL((ep::combine_kernel<16, kCombineUnroll, kCombineWaves, kCombineNtLoad, kCombineNtStore>),
+                       cgrid, block, 0, s, yv, pos, weights, ov, T, K, V, chunks, cap_rows);
   return launch_status("ep_combine");
 }
 
@@ -494,23 +500,24 @@ EP_EXPORT int ep_combine_quant(int32_t T, int32_t K, int32_t H, const void* code
   const int NG = H / 16;
   const int chunks = (NG + ep::kWave - 1) / ep::kWave;
   const int64_t items = (int64_t)T * chunks;
-  if ((items + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock > INT32_MAX)
+  if ((items + kCombineQuantWaves - 1) / kCombineQuantWaves > INT32_MAX)
     return fail(EP_ERR_UNSUPPORTED, "T * H too large for one launch");
-  const dim3 grid((unsigned)((items + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock)), block(ep::kRowThreads);
+  const dim3 grid((unsigned)((items + kCombineQuantWaves - 1) / kCombineQuantWaves));
+  const dim3 block(kCombineQuantWaves * ep::kWave);
   hipStream_t s = (hipStream_t)stream;
   const ep::u32x4* cv = (const ep::u32x4*)codes;
   ep::u32x4* ov = (ep::u32x4*)out;
   auto launch = [&](auto qt) {
     constexpr int QT = decltype(qt)::value;
     if (K <= 4)
-      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 4, kCombineNtLoad, kCombineNtStore>), grid, block, 0, s, cv,
-                         row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
+      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 4, kCombineQuantWaves, kCombineNtLoad, kCombineNtStore>), grid,
+                         block, 0, s, cv, row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
     else if (K <= 8)
-      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 8, kCombineNtLoad, kCombineNtStore>), grid, block, 0, s, cv,
-                         row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
+      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 8, kCombineQuantWaves, kCombineNtLoad, kCombineNtStore>), grid,
+                         block, 0, s, cv, row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
     else
-      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 16, kCombineNtLoad, kCombineNtStore>), grid, block, 0, s, cv,
-                         row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
+      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 16, kCombineQuantWaves, kCombineNtLoad, kCombineNtStore>), grid,
+                         block, 0, s, cv, row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
   };
   if (code_dtype == EP_FP8_E4M3FN) launch(std::integral_constant<int, ep::kQFp8>{});
   else launch(std::integral_constant<int, ep::kQInt8>{});

@@ -334,12 +334,12 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_quant_kernel(
 // vectors); all K row chunks are loaded before the first FMA so the K
 // gathers are in flight together.
 // ---------------------------------------------------------------------------
-template <int KMAX, int U, bool NTL, bool NTS>
-__global__ __launch_bounds__(kRowThreads) void combine_kernel(
+template <int KMAX, int U, int WPB, bool NTL, bool NTS>
+__global__ __launch_bounds__(WPB * kWave) void combine_kernel(
     const u32x4* __restrict__ y, const int32_t* __restrict__ pos,
     const float* __restrict__ w, u32x4* __restrict__ out, int T, int K, int V, int chunks,
     int64_t cap_rows) {
-  const int64_t g = (int64_t)blockIdx.x * kTokensPerBlock + uniform((int)(threadIdx.x / kWave));
+  const int64_t g = (int64_t)blockIdx.x * WPB + uniform((int)(threadIdx.x / kWave));
   const int64_t t64 = g / chunks;
   if (t64 >= T) return;
   const int t = (int)t64;
@@ -508,12 +508,12 @@ __device__ __forceinline__ void decode4(uint32_t c, float* v) {
   }
 }
 
-template <int QT, int KMAX, bool NTL, bool NTS>
-__global__ __launch_bounds__(kRowThreads) void combine_quant_kernel(
+template <int QT, int KMAX, int WPB, bool NTL, bool NTS>
+__global__ __launch_bounds__(WPB * kWave) void combine_quant_kernel(
     const u32x4* __restrict__ codes, const float* __restrict__ row_scales,
     const int32_t* __restrict__ pos, const float* __restrict__ w, u32x4* __restrict__ out, int T,
     int K, int NG, int chunks, int64_t cap_rows) {
-  const int64_t g = (int64_t)blockIdx.x * kTokensPerBlock + uniform((int)(threadIdx.x / kWave));
+  const int64_t g = (int64_t)blockIdx.x * WPB + uniform((int)(threadIdx.x / kWave));
   const int64_t t64 = g / chunks;
   if (t64 >= T) return;
   const int t = (int)t64;
