@@ -571,18 +571,18 @@ __global__ __launch_bounds__(WPB * kWave) void combine_quant_kernel(
 // the all-reduce; CombineAddRmsNorm on the CANN dispatch page):
 //   c = bf16(sum_k w[t][k] y[pos[t][k]]),  h = bf16(residual[t] + c),
 //   norm = bf16(h * gamma / sqrt(mean(h^2) + eps)).
-// One workgroup per token; thread i owns the 16-byte vectors i, i + 256, ...
-// (NV of them, H <= NV * 2048), whose h values stay in VGPRs between the
-// sum-of-squares pass and the scaling pass.  The combined rows never go
-// to HBM.  With y == nullptr the kernel is the tail alone: c = x[t].
+// One NT-thread workgroup per token; thread i owns the 16-byte vectors i,
+// i + NT, ... (NV of them, H <= NV * NT * 8), whose h values stay in VGPRs
+// between the sum-of-squares pass and the scaling pass.  The combined rows
+// never go to HBM.  With y == nullptr the kernel is the tail alone: c = x[t].
 // ---------------------------------------------------------------------------
-template <int KMAX, int NV, bool NTL, bool NTS>
-__global__ __launch_bounds__(kRowThreads) void combine_add_rmsnorm_kernel(
+template <int KMAX, int NV, int NT, bool NTL, bool NTS>
+__global__ __launch_bounds__(NT) void combine_add_rmsnorm_kernel(
     const u32x4* __restrict__ y, const int32_t* __restrict__ pos, const float* __restrict__ w,
     const u32x4* __restrict__ x, const u32x4* __restrict__ residual, const u32x4* __restrict__ gamma,
     float eps, u32x4* __restrict__ residual_out, u32x4* __restrict__ norm_out, int T, int K, int V,
     int64_t cap_rows) {
-  __shared__ float s_sum[kRowThreads / kWave];
+  __shared__ float s_sum[NT / kWave];
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(kRowThreads) void combine_add_rmsnorm_kernel(
   float sumsq = 0.0f;
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int v = tid + i * kRowThreads;
+    const int v = tid + i * NT;
     if (v < V) {
       float c[8];
       if (y != nullptr) {
@@ -661,11 +661,11 @@ __global__ __launch_bounds__(kRowThreads) void combine_add_rmsnorm_kernel(
   __syncthreads();
   float total = 0.0f;
 #pragma unroll
-  for (int q = 0; q < kRowThreads / kWave; ++q) total += s_sum[q];
+  for (int q = 0; q < NT / kWave; ++q) total += s_sum[q];
   const float inv = 1.0f / sqrtf(total / (float)(V * 8) + eps);
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
-    const int v = tid + i * kRowThreads;
+    const int v = tid + i * NT;
     if (v < V) {
       const u32x4 gv = gamma[v];
       const uint32_t g4[4] = {gv.x, gv.y, gv.z, gv.w};
