@@ -37,12 +37,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # the kernels built from the sources whose digest is `source_sha256`; any
 # other build reports traffic as null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "1db59e6f40bb4ea93c2c8994aaa36054c9b4dc11f026ffd1e50efb7ce6757623",
+    "source_sha256": "0246de8f250a47538b35a58969e84358bc8ffced701ea83ea0c32096687bdc29",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "2": {"ep_plan": 1938425, "ep_dispatch": 1059659374, "ep_combine": 1061186748, "ep_dispatch_smooth": 875929187, "ep_combine_quant": 600525509, "ep_combine_add_rmsnorm": 1294293065, "ep_add_rmsnorm": 470058844},
-        "4": {"ep_plan": 3561170, "ep_dispatch": 885904546, "ep_combine": 1652684813, "ep_dispatch_smooth": 2301777536, "ep_combine_quant": 969457219, "ep_combine_add_rmsnorm": 2118578239, "ep_add_rmsnorm": 939813633},
-        "1": {"ep_plan": 652724, "ep_dispatch": 235760941, "ep_combine": 236502921, "ep_dispatch_smooth": 144420743, "ep_combine_quant": 138612913},
-        "3": {"ep_plan_splits": 6144, "ep_dispatch_splits": 268555528},
+        "2": {"ep_plan": 1952880, "ep_dispatch": 1059684508, "ep_combine": 1061195184, "ep_dispatch_smooth": 875725126, "ep_combine_quant": 600894655, "ep_combine_add_rmsnorm": 1294119184, "ep_add_rmsnorm": 469930861},
+        "4": {"ep_plan": 3572434, "ep_dispatch": 885907709, "ep_combine": 1652693243, "ep_dispatch_smooth": 2301820982, "ep_combine_quant": 968794539, "ep_combine_add_rmsnorm": 2118405846, "ep_add_rmsnorm": 939685631},
+        "1": {"ep_plan": 660620, "ep_dispatch": 235760467, "ep_combine": 236511199, "ep_dispatch_smooth": 144420239, "ep_combine_quant": 138652773},
+        "3": {"ep_plan_splits": 6144, "ep_dispatch_splits": 268563265},
     },
 }
 
