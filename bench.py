@@ -6,7 +6,9 @@ One step is the whole hot path over one batch of resident synthetic input:
 ep_plan (split counts, scans, exchange plan, stable positions) -> ep_dispatch
 (scatter into the expert-grouped expandX buffer; per-token fp8 for the fp8
 workload) -> ep_combine (weighted gather of the K expert rows per token).
-The uneven all-to-all workload times ep_plan_splits -> ep_dispatch_splits.
+The uneven all-to-all workload times ep_all_to_all_splits (plan and data move
+in one launch), with the two-launch form ep_plan_splits -> ep_dispatch_splits
+timed beside it.
 
 Prints one JSON line: whole-job tokens/s, the step's algorithmic HBM GB/s,
 a roofline record for the dominant kernel (its algorithmic bytes per launch
@@ -304,11 +306,14 @@ class SplitsBench:
         self.out = torch.empty((cfg.W * cfg.R, cfg.H), dtype=torch.int16, device="cuda")
 
     def phases(self):
-        return [("ep_plan_splits", lambda: self.ep.ep_plan_splits(self.send, self.sp)),
-                ("ep_dispatch_splits", lambda: self.ep.ep_dispatch_splits(self.inp, self.sp, self.out))]
+        """One launch: the plan and the data move fused (ep_all_to_all_splits)."""
+        return [("ep_all_to_all_splits",
+                 lambda: self.ep.ep_all_to_all_splits(self.send, self.inp, self.out, self.sp))]
 
     def extra_phases(self):
-        return []
+        """The two-launch form timed beside it: plan, then move."""
+        return [("ep_plan_splits", lambda: self.ep.ep_plan_splits(self.send, self.sp)),
+                ("ep_dispatch_splits", lambda: self.ep.ep_dispatch_splits(self.inp, self.sp, self.out))]
 
     def n_rows(self):
         return self.cfg.W * self.cfg.R
@@ -317,7 +322,8 @@ class SplitsBench:
         c = self.cfg
         W = c.W
         return {"ep_plan_splits": W * W * 8 * 4 + (W + 1) * 8,
-                "ep_dispatch_splits": 2 * N * c.H * 2 + 4 * W * W * 8}
+                "ep_dispatch_splits": 2 * N * c.H * 2 + 4 * W * W * 8,
+                "ep_all_to_all_splits": 2 * N * c.H * 2 + W * W * 8 * 4 + (W + 1) * 8}
 
     def tokens(self):
         return self.cfg.W * self.cfg.R   # rows moved

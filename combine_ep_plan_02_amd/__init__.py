@@ -43,7 +43,8 @@ _STATUS_NAMES = {1: "EP_ERR_NULLPTR", 2: "EP_ERR_INVALID", 3: "EP_ERR_UNSUPPORTE
 EXPORTED = ("ep_supported", "ep_workspace_size", "ep_workspace_init", "ep_expand_rows_bound",
             "ep_plan", "ep_dispatch", "ep_dispatch_smooth", "ep_combine", "ep_combine_quant",
             "ep_combine_add_rmsnorm", "ep_add_rmsnorm",
-            "ep_plan_splits", "ep_dispatch_splits", "ep_last_error", "ep_device_error")
+            "ep_plan_splits", "ep_dispatch_splits", "ep_all_to_all_splits", "ep_last_error",
+            "ep_device_error")
 
 
 class EPError(RuntimeError):
@@ -87,6 +88,7 @@ def _load() -> ctypes.CDLL:
         "ep_add_rmsnorm": ([i32, i32, P, P, P, ctypes.c_float, P, P, P], ctypes.c_int),
         "ep_plan_splits": ([i32, P, P, P, P, P, P], ctypes.c_int),
         "ep_dispatch_splits": ([i32, i64, i64, P, P, P, P, P, P, P], ctypes.c_int),
+        "ep_all_to_all_splits": ([i32, i64, i64, P, P, P, P, P, P, P, P], ctypes.c_int),
         "ep_last_error": ([], ctypes.c_char_p),
         "ep_device_error": ([P, ctypes.POINTER(ctypes.c_int32)], ctypes.c_int),
     }
@@ -368,6 +370,23 @@ def ep_dispatch_splits(inp: torch.Tensor, plan: SplitsPlan, out: torch.Tensor, s
                                   _ptr(plan.dst_offsets, torch.int64, "dst_offsets"),
                                   _ptr(plan.rank_offsets, torch.int64, "rank_offsets"),
                                   _ptr(out, name="out"), _stream(stream)))
+
+
+def ep_all_to_all_splits(in_splits: torch.Tensor, inp: torch.Tensor, out: torch.Tensor,
+                         plan: SplitsPlan | None = None, stream=None) -> None:
+    """Plan and data move of the 1-D all-to-all in one launch; fills `plan`
+    (optional) with what ep_plan_splits computes."""
+    W, R = inp.shape[:2]
+    if tuple(in_splits.shape) != (W, W):
+        raise ValueError("in_splits must be [W][W]")
+    stride = inp[0, 0].numel() * inp.element_size() if R else 16
+    if out.shape[0] != W * R or (R and out[0].numel() * out.element_size() != stride):
+        raise ValueError("out must hold W*R rows of the input's row size")
+    g = (lambda f: _ptr(getattr(plan, f), torch.int64, f)) if plan is not None else (lambda f: None)
+    _check(lib.ep_all_to_all_splits(W, R, stride, _ptr(in_splits, torch.int64, "in_splits"),
+                                    _ptr(inp, name="in"), _ptr(out, name="out"), g("src_offsets"),
+                                    g("out_splits"), g("dst_offsets"), g("rank_offsets"),
+                                    _stream(stream)))
 
 
 def ep_device_error(stream=None) -> int:

@@ -696,6 +696,57 @@ EP_EXPORT int ep_dispatch_splits(int32_t W, int64_t R, int64_t stride_bytes, con
   return launch_status("ep_dispatch_splits");
 }
 
+EP_EXPORT int ep_all_to_all_splits(int32_t W, int64_t R, int64_t stride_bytes, const int64_t* in_splits,
+                                   const void* in, void* out, int64_t* src_offsets, int64_t* out_splits,
+                                   int64_t* dst_offsets, int64_t* rank_offsets, void* stream) {
+  if (W < 1 || W > EP_MAX_SPLITS_W)
+    return fail(EP_ERR_UNSUPPORTED, "W must be in [1, %d] (got %d)", EP_MAX_SPLITS_W, W);
+  if (R < 0) return fail(EP_ERR_INVALID, "R must be >= 0");
+  if (stride_bytes <= 0 || stride_bytes % 16)
+    return fail(EP_ERR_UNSUPPORTED, "stride_bytes must be a positive multiple of 16 (got %lld)",
+                (long long)stride_bytes);
+  const bool any_plan = src_offsets || out_splits || dst_offsets || rank_offsets;
+  if (R == 0 && !any_plan) return ok();
+  if (!in_splits) return fail(EP_ERR_NULLPTR, "in_splits is required");
+  if (R > 0 && (!in || !out)) return fail(EP_ERR_NULLPTR, "in and out are required");
+  if (R > 0 && (!aligned(in, 16) || !aligned(out, 16)))
+    return fail(EP_ERR_INVALID, "in and out must be 16-byte aligned");
+  const size_t bytes = (size_t)W * R * stride_bytes;
+  const size_t mb = (size_t)W * W * 8;
+  const void* arrays[] = {in_splits, src_offsets, out_splits, dst_offsets, rank_offsets, in, out};
+  const size_t sizes[] = {mb, mb, mb, mb, (size_t)(W + 1) * 8, bytes, bytes};
+  for (int i = 0; i < 5; ++i)
+    if (arrays[i] && !aligned(arrays[i], 8)) return fail(EP_ERR_INVALID, "split arrays must be 8-byte aligned");
+  // outputs (1-4, 6) must not overlap each other or an input (0, 5)
+  for (int i = 0; i < 7; ++i)
+    for (int j = i + 1; j < 7; ++j) {
+      const bool out_i = i != 0 && i != 5, out_j = j != 0 && j != 5;
+      if ((out_i || out_j) && arrays[i] && arrays[j] && sizes[i] && sizes[j] &&
+          overlap(arrays[i], sizes[i], arrays[j], sizes[j]))
+        return fail(EP_ERR_INVALID, "an output of the all-to-all overlaps another buffer");
+    }
+  const int64_t Vr = stride_bytes / 16;
+  const int chunks = W * W;
+  int bpc = (2048 + chunks - 1) / chunks;
+  const int64_t need = (R + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock;
+  if (bpc > need) bpc = (int)need;
+  if (bpc < 1) bpc = 1;
+  const dim3 grid(chunks, bpc);
+  hipStream_t s = (hipStream_t)stream;
+  const ep::u32x4* iv = (const ep::u32x4*)in;
+  ep::u32x4* ov = (ep::u32x4*)out;
+  const int64_t per_lane = (Vr + ep::kWave - 1) / ep::kWave;
+#define EP_A2A(U)                                                                                          \
+  hipLaunchKernelGGL((ep::all_to_all_splits_kernel<U, kCopyNtLoad, kCopyNtStore>), grid, dim3(ep::kRowThreads), \
+                     0, s, iv, ov, in_splits, src_offsets, out_splits, dst_offsets, rank_offsets, W, R, Vr)
+  if (per_lane <= 1) EP_A2A(1);
+  else if (per_lane <= 2) EP_A2A(2);
+  else if (per_lane <= 4) EP_A2A(4);
+  else EP_A2A(8);
+#undef EP_A2A
+  return launch_status("ep_all_to_all_splits");
+}
+
 EP_EXPORT const char* ep_last_error(void) { return g_last_error.c_str(); }
 
 EP_EXPORT int ep_device_error(void* stream, int32_t* code) {

@@ -759,4 +759,87 @@ __global__ __launch_bounds__(kRowThreads) void copy_splits_kernel(
   }
 }
 
+// The plan and the data move of the 1-D all-to-all in one launch.  Same grid
+// as copy_splits_kernel; each workgroup first derives its own chunk's plan
+// entries from the send matrix in_splits[p][r] (W*W values, read through
+// the cache by every workgroup): its threads split the matrix and reduce
+//   src  = sum_{r' < r} in_splits[p][r']          (row in p's input)
+//   dst  = sum_{p' < p} in_splits[p'][r]          (row in r's output)
+//   base = sum_{r' < r} sum_{p'} in_splits[p'][r'] (rank_offsets[r])
+// and the total (rank_offsets[W]).  The y == 0 workgroup of each chunk
+// writes the chunk's plan entries to the optional outputs.
+template <int U, bool NTL, bool NTS>
+__global__ __launch_bounds__(kRowThreads) void all_to_all_splits_kernel(
+    const u32x4* __restrict__ in, u32x4* __restrict__ out, const int64_t* __restrict__ in_splits,
+    int64_t* __restrict__ src_offsets, int64_t* __restrict__ out_splits, int64_t* __restrict__ dst_offsets,
+    int64_t* __restrict__ rank_offsets, int W, int64_t R, int64_t Vr) {
+  __shared__ int64_t part[4][kRowThreads / kWave];
+  const int q = blockIdx.x;
+  const int r = q / W, p = q - r * W;
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  int64_t a_src = 0, a_dst = 0, a_base = 0, a_tot = 0;
+  for (int e = tid; e < W * W; e += kRowThreads) {
+    const int pp = e / W, rr = e - pp * W;
+    const int64_t v = in_splits[e];
+    if (pp == p && rr < r) a_src += v;
+    if (rr == r && pp < p) a_dst += v;
+    if (rr < r) a_base += v;
+    a_tot += v;
+  }
+#pragma unroll
+  for (int off = kWave / 2; off > 0; off >>= 1) {
+    a_src += __shfl_xor(a_src, off, kWave);
+    a_dst += __shfl_xor(a_dst, off, kWave);
+    a_base += __shfl_xor(a_base, off, kWave);
+    a_tot += __shfl_xor(a_tot, off, kWave);
+  }
+  if (lane == 0) {
+    part[0][wave] = a_src;
+    part[1][wave] = a_dst;
+    part[2][wave] = a_base;
+    part[3][wave] = a_tot;
+  }
+  __syncthreads();
+  int64_t src = 0, dsub = 0, base = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kRowThreads / kWave; ++w) {
+    src += part[0][w];
+    dsub += part[1][w];
+    base += part[2][w];
+    tot += part[3][w];
+  }
+  const int64_t n = in_splits[(int64_t)p * W + r];
+  if (blockIdx.y == 0 && tid == 0) {
+    if (out_splits) out_splits[q] = n;
+    if (src_offsets) src_offsets[q] = src;
+    if (dst_offsets) dst_offsets[q] = dsub;
+    if (rank_offsets && p == 0) rank_offsets[r] = base;
+    if (rank_offsets && q == 0) rank_offsets[W] = tot;
+  }
+  const int64_t dst = base + dsub;
+  if (n == 0) return;
+  if (n < 0 || src < 0 || src + n > R || dst < 0 || dst + n > (int64_t)W * R) {
+    if (blockIdx.y == 0 && tid == 0) raise_device_error(kErrSplits);
+    return;
+  }
+  const int64_t step = (int64_t)gridDim.y * kTokensPerBlock;
+  for (int64_t i = (int64_t)blockIdx.y * kTokensPerBlock + wave; i < n; i += step) {
+    const u32x4* s = in + ((int64_t)p * R + src + i) * Vr;
+    u32x4* d = out + (dst + i) * Vr;
+    for (int64_t v0 = 0; v0 < Vr; v0 += kWave * U) {
+      u32x4 t[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t idx = v0 + u * kWave + lane;
+        if (idx < Vr) t[u] = ld<NTL>(s + idx);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int64_t idx = v0 + u * kWave + lane;
+        if (idx < Vr) st<NTS>(d + idx, t[u]);
+      }
+    }
+  }
+}
+
 }  // namespace ep

@@ -294,6 +294,19 @@ int ep_dispatch_splits(int32_t W, int64_t R, int64_t stride_bytes, const void *i
                        const int64_t *dst_offsets, const int64_t *rank_offsets, void *out,
                        void *stream);
 
+/* The 1-D all-to-all in one launch: ep_plan_splits and ep_dispatch_splits
+ * fused (every workgroup derives its own chunk's offsets from in_splits
+ * [W][W], so no plan kernel runs first).  Moves the rows exactly as
+ * ep_dispatch_splits does with the plan ep_plan_splits computes, and writes
+ * that plan to src_offsets / out_splits / dst_offsets ([W][W]) and
+ * rank_offsets ([W+1]), each of which may be NULL (not written).  A chunk
+ * whose rows fall outside the buffers is skipped and sets
+ * EP_DEVERR_SPLITS.  R == 0 with no plan output requested enqueues
+ * nothing; in and out may be NULL when R == 0. */
+int ep_all_to_all_splits(int32_t W, int64_t R, int64_t stride_bytes, const int64_t *in_splits,
+                         const void *in, void *out, int64_t *src_offsets, int64_t *out_splits,
+                         int64_t *dst_offsets, int64_t *rank_offsets, void *stream);
+
 /* Thread-local description of the last non-OK status ("" if none). */
 const char *ep_last_error(void);
 

@@ -130,6 +130,13 @@ int main(void)
     expect(ep_dispatch_splits(8, 4096, 4100, P(28 * G), so, os, dof, ro64, P(29 * G), NULL), EP_ERR_UNSUPPORTED, "splits stride");
     expect(ep_dispatch_splits(8, 0, 4096, NULL, so, os, dof, ro64, NULL, NULL), EP_OK, "splits empty");
 
+    /* 1-D all-to-all in one launch */
+    const int64_t *isp = (const int64_t *)P(30 * G);
+    expect(ep_all_to_all_splits(65, 16, 32, isp, P(28 * G), P(29 * G), so, os, dof, ro64, NULL), EP_ERR_UNSUPPORTED, "fused splits W");
+    expect(ep_all_to_all_splits(8, 16, 32, NULL, P(28 * G), P(29 * G), so, os, dof, ro64, NULL), EP_ERR_NULLPTR, "fused splits NULL");
+    expect(ep_all_to_all_splits(8, 16, 32, isp, P(28 * G), P(28 * G) , NULL, NULL, NULL, NULL, NULL), EP_ERR_INVALID, "fused splits alias");
+    expect(ep_all_to_all_splits(8, 0, 32, NULL, NULL, NULL, NULL, NULL, NULL, NULL, NULL), EP_OK, "fused splits empty");
+
     /* a long message does not overflow the error buffer */
     expect(ep_dispatch(64, 2, 128, x, pos, EP_BF16, ex, NULL, NULL, NULL, -9223372036854775807LL, NULL),
            EP_ERR_INVALID, "dispatch negative cap");

@@ -252,3 +252,18 @@ def test_combine_quant_rejections(ep):
     assert c(64, 2, 128, Q, F8, S, 128, P, Wt, Q + 512, None) == ep.EP_ERR_INVALID  # out over codes
     assert c(64, 2, 128, Q, F8, S, -1, P, Wt, O, None) == ep.EP_ERR_INVALID
     assert c(0, 2, 128, None, F8, None, 0, None, None, None, None) == ep.EP_OK
+
+
+def test_fused_splits_rejections(ep):
+    f = ep.lib.ep_all_to_all_splits
+    S, I, O, P1, P2, P3, P4 = (A + (i << 34) for i in range(7))
+    assert f(65, 16, 32, S, I, O, P1, P2, P3, P4, None) == ep.EP_ERR_UNSUPPORTED   # W > 64
+    assert f(8, -1, 32, S, I, O, P1, P2, P3, P4, None) == ep.EP_ERR_INVALID        # R < 0
+    assert f(8, 16, 40, S, I, O, P1, P2, P3, P4, None) == ep.EP_ERR_UNSUPPORTED    # stride % 16
+    assert f(8, 16, 32, None, I, O, P1, P2, P3, P4, None) == ep.EP_ERR_NULLPTR     # in_splits
+    assert f(8, 16, 32, S, None, O, None, None, None, None, None) == ep.EP_ERR_NULLPTR
+    assert f(8, 16, 32, S, I + 8, O, None, None, None, None, None) == ep.EP_ERR_INVALID  # alignment
+    assert f(8, 16, 32, S, I, I + 64, None, None, None, None, None) == ep.EP_ERR_INVALID  # out over in
+    assert f(8, 16, 32, S, I, O, P1, P1 + 8, None, None, None) == ep.EP_ERR_INVALID    # plan arrays overlap
+    assert f(8, 16, 32, S, I, O, S, None, None, None, None) == ep.EP_ERR_INVALID       # plan over in_splits
+    assert f(8, 0, 32, None, None, None, None, None, None, None, None) == ep.EP_OK     # nothing to do

@@ -313,3 +313,88 @@ def test_splits_config3_full():
     want_out, err = oracle.a2a_copy(inp, want)
     assert err == 0
     assert (host(out, np.uint16) == want_out).all()
+
+
+# ------------------------------------------- 1-D all-to-all in one launch
+
+def run_fused_splits(send, inp, with_plan=True):
+    W = send.shape[0]
+    sp = ep.alloc_splits_plan(W) if with_plan else None
+    if sp is not None:
+        for f in ("src_offsets", "out_splits", "dst_offsets", "rank_offsets"):
+            getattr(sp, f).fill_(-7)
+    out = torch.full((inp.shape[0] * inp.shape[1],) + inp.shape[2:], -1,
+                     dtype=torch.int32 if inp.dtype == np.int32 else torch.int16, device="cuda")
+    ep.ep_all_to_all_splits(dev(send.astype(np.int64)), dev(inp), out, sp)
+    return sp, out
+
+
+def test_fused_splits_worked_example():
+    say("fused splits worked example")
+    send = np.array([[1, 3], [2, 2]], np.int64)
+    inp = np.zeros((2, 4, 8), np.int32)
+    for i in range(2):
+        for k in range(4):
+            inp[i, k] = 10 * i + k
+    sp, out = run_fused_splits(send, inp)
+    o = host(out)
+    assert o[0:3, 0].tolist() == [0, 10, 11]
+    assert o[3:8, 0].tolist() == [1, 2, 3, 12, 13]
+    want = oracle.a2a_plan(send)
+    for f in ("src_offsets", "out_splits", "dst_offsets", "rank_offsets"):
+        assert (host(getattr(sp, f)) == getattr(want, f)).all(), f
+    assert ep.ep_device_error() == 0
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_fused_splits_random(seed):
+    rng = np.random.default_rng(100 + seed)
+    W = int([1, 3, 8, 64, 17][seed])
+    R = int(rng.integers(1, 300))
+    send = np.zeros((W, W), np.int64)
+    for p in range(W):
+        cuts = np.sort(rng.integers(0, R + 1, W - 1))
+        send[p] = np.diff(np.concatenate([[0], cuts, [R]]))
+    send[W - 1, :] = 0
+    send[W - 1, 0] = R                       # zero-row chunks
+    inp = rng.integers(0, 1 << 16, size=(W, R, 40)).astype(np.uint16)
+    say("fused splits random W", W, "R", R)
+    sp, out = run_fused_splits(send, inp, with_plan=seed != 2)
+    want = oracle.a2a_plan(send)
+    want_out, err = oracle.a2a_copy(inp, want, fill=0xFFFF)
+    assert err == 0
+    assert (host(out, np.uint16) == want_out).all()
+    if sp is not None:
+        for f in ("src_offsets", "out_splits", "dst_offsets", "rank_offsets"):
+            assert (host(getattr(sp, f)) == getattr(want, f)).all(), f
+    assert ep.ep_device_error() == 0
+
+
+def test_fused_splits_bad_matrix_is_flagged():
+    """A row sum above R: the chunks that would read past a sender's R rows
+    are skipped and flagged, as ep_dispatch_splits does with the same plan."""
+    say("fused splits, send matrix past R")
+    send = np.array([[1, 3], [2, 4]], np.int64)   # rank 1 sends 6 rows, has 4
+    inp = np.arange(2 * 4 * 8, dtype=np.int32).reshape(2, 4, 8)
+    sp, out = run_fused_splits(send, inp)
+    assert ep.ep_device_error() == ep.EP_DEVERR_SPLITS
+    want = oracle.a2a_plan(send)
+    for f in ("src_offsets", "out_splits", "dst_offsets", "rank_offsets"):
+        assert (host(getattr(sp, f)) == getattr(want, f)).all(), f
+    # the oracle's copy of the same plan skips the same chunks
+    want_out, err = oracle.a2a_copy(inp, want, fill=-1)
+    assert err == oracle.DEVERR_SPLITS
+    assert (host(out) == want_out).all()
+
+
+def test_fused_splits_config3_full():
+    cfg = workloads.WORKLOADS[3]
+    say("fused splits config 3 full", cfg)
+    send, inp = workloads.splits_inputs(cfg)
+    sp, out = run_fused_splits(send, inp)
+    want = oracle.a2a_plan(send)
+    want_out, err = oracle.a2a_copy(inp, want)
+    assert err == 0
+    assert (host(out, np.uint16) == want_out).all()
+    for f in ("src_offsets", "out_splits", "dst_offsets", "rank_offsets"):
+        assert (host(getattr(sp, f)) == getattr(want, f)).all(), f
