@@ -39,12 +39,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # the kernels built from the sources whose digest is `source_sha256`; any
 # other build reports traffic as null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "0246de8f250a47538b35a58969e84358bc8ffced701ea83ea0c32096687bdc29",
+    "source_sha256": "63a3c83f23e8f01ab32d17903c7af1c9a068d481e0c58189821a5de28d1207f4",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "2": {"ep_plan": 1952880, "ep_dispatch": 1059684508, "ep_combine": 1061195184, "ep_dispatch_smooth": 875725126, "ep_combine_quant": 600894655, "ep_combine_add_rmsnorm": 1294119184, "ep_add_rmsnorm": 469930861},
-        "4": {"ep_plan": 3572434, "ep_dispatch": 885907709, "ep_combine": 1652693243, "ep_dispatch_smooth": 2301820982, "ep_combine_quant": 968794539, "ep_combine_add_rmsnorm": 2118405846, "ep_add_rmsnorm": 939685631},
-        "1": {"ep_plan": 660620, "ep_dispatch": 235760467, "ep_combine": 236511199, "ep_dispatch_smooth": 144420239, "ep_combine_quant": 138652773},
-        "3": {"ep_plan_splits": 6144, "ep_dispatch_splits": 268563265},
+        "2": {"ep_plan": 1940484, "ep_dispatch": 1059664268, "ep_combine": 1061189647, "ep_dispatch_smooth": 876010774, "ep_combine_quant": 601025369, "ep_combine_add_rmsnorm": 1294122163, "ep_add_rmsnorm": 469946146},
+        "4": {"ep_plan": 3554272, "ep_dispatch": 885937658, "ep_combine": 1652689040, "ep_dispatch_smooth": 2301263416, "ep_combine_quant": 969102088, "ep_combine_add_rmsnorm": 2118412044, "ep_add_rmsnorm": 939702216},
+        "1": {"ep_plan": 654549, "ep_dispatch": 235764667, "ep_combine": 236503322, "ep_dispatch_smooth": 144422368, "ep_combine_quant": 138710886},
+        "3": {"ep_all_to_all_splits": 268558971, "ep_plan_splits": 5920, "ep_dispatch_splits": 268564747},
     },
 }
 
