@@ -186,6 +186,13 @@ class MoEBench:
         self.ep.ep_combine_quant(self.qx, self.qs, self.plan.pos, self.w, self.out,
                                  code_dtype=self.ep.EP_FP8_E4M3FN)
 
+    def dispatch_int8_step(self):
+        self.ep.ep_dispatch(self.x, self.plan.pos, self.qx, self.qs, out_dtype=self.ep.EP_INT8)
+
+    def combine_int8_step(self):
+        self.ep.ep_combine_quant(self.qx, self.qs, self.plan.pos, self.w, self.out,
+                                 code_dtype=self.ep.EP_INT8)
+
     def phases(self):
         last = ("ep_combine_add_rmsnorm", self.tail_step) if self.tail else \
             ("ep_combine", self.combine_step)
@@ -193,10 +200,12 @@ class MoEBench:
 
     def extra_phases(self):
         """Kernels timed beside the step: the quantisation variants (smoothed
-        fp8 dispatch, combine of fp8 expert rows) and, with the tail, the
-        unfused tail pair."""
+        fp8 dispatch, combine of fp8 expert rows, int8 dispatch and combine of
+        int8 rows) and, with the tail, the unfused tail pair."""
         ph = [("ep_dispatch_smooth", self.dispatch_smooth_step),
-              ("ep_combine_quant", self.combine_quant_step)]
+              ("ep_combine_quant", self.combine_quant_step),
+              ("ep_dispatch_int8", self.dispatch_int8_step),
+              ("ep_combine_quant_int8", self.combine_int8_step)]
         if self.tail:
             ph += [("ep_combine", self.combine_step), ("ep_add_rmsnorm", self.add_rmsnorm_step)]
         return ph
@@ -223,7 +232,9 @@ class MoEBench:
         combq_b = N * (c.H + 4) + c.T * 2 * c.H + tk * 4 * 2
         return {"ep_plan": plan_b, "ep_dispatch": disp_b, "ep_combine": comb_b,
                 "ep_combine_add_rmsnorm": tail_b, "ep_add_rmsnorm": addn_b,
-                "ep_dispatch_smooth": smooth_b, "ep_combine_quant": combq_b}
+                "ep_dispatch_smooth": smooth_b, "ep_combine_quant": combq_b,
+                "ep_dispatch_int8": self.live_tokens * row_in + N * (c.H + 4) + tk * 4,
+                "ep_combine_quant_int8": combq_b}
 
     def tokens(self):
         return self.cfg.T
