@@ -41,10 +41,10 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 TRAFFIC = {
     "source_sha256": "63a3c83f23e8f01ab32d17903c7af1c9a068d481e0c58189821a5de28d1207f4",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "2": {"ep_plan": 1940484, "ep_dispatch": 1059664268, "ep_combine": 1061189647, "ep_dispatch_smooth": 876010774, "ep_combine_quant": 601025369, "ep_combine_add_rmsnorm": 1294122163, "ep_add_rmsnorm": 469946146},
-        "4": {"ep_plan": 3554272, "ep_dispatch": 885937658, "ep_combine": 1652689040, "ep_dispatch_smooth": 2301263416, "ep_combine_quant": 969102088, "ep_combine_add_rmsnorm": 2118412044, "ep_add_rmsnorm": 939702216},
-        "1": {"ep_plan": 654549, "ep_dispatch": 235764667, "ep_combine": 236503322, "ep_dispatch_smooth": 144422368, "ep_combine_quant": 138710886},
-        "3": {"ep_all_to_all_splits": 268558971, "ep_plan_splits": 5920, "ep_dispatch_splits": 268564747},
+        "2": {"ep_plan": 1944444, "ep_dispatch": 1059731112, "ep_combine": 1061189362, "ep_dispatch_smooth": 876082137, "ep_combine_quant": 600762250, "ep_dispatch_int8": 590460090, "ep_combine_quant_int8": 600770634, "ep_combine_add_rmsnorm": 1294122011, "ep_add_rmsnorm": 469946107},
+        "4": {"ep_plan": 3565271, "ep_dispatch": 885915550, "ep_combine": 1652688803, "ep_dispatch_smooth": 2300942391, "ep_combine_quant": 969356912, "ep_dispatch_int8": 885965463, "ep_combine_quant_int8": 968719952, "ep_combine_add_rmsnorm": 2118411857, "ep_add_rmsnorm": 939702138},
+        "1": {"ep_plan": 651189, "ep_dispatch": 235766790, "ep_combine": 236503264, "ep_dispatch_smooth": 144420281, "ep_combine_quant": 138964789, "ep_dispatch_int8": 135604468, "ep_combine_quant_int8": 138717716},
+        "3": {"ep_all_to_all_splits": 268562925, "ep_plan_splits": 5920, "ep_dispatch_splits": 268574485},
     },
 }
 
