@@ -87,8 +87,8 @@ def log(*a):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4],
                     help="index of the workload (2: T=8192 H=7168 E=256 K=8 W=16 Zipf; "
                          "0: the T=64 latency case)")
@@ -524,7 +524,13 @@ def main():
         rec["live_tokens_per_s"] = live / (ms_per_step * 1e-3)
     if not args.no_cpu_baseline:
         log("[bench] CPU oracle baseline")
-        rec["cpu_baseline"] = bench.cpu_baseline(args.cpu_reps) | host_cpu()
+        # the serial oracle runs pinned to one of the process's cores
+        allowed = os.sched_getaffinity(0)
+        os.sched_setaffinity(0, {min(allowed)})
+        try:
+            rec["cpu_baseline"] = bench.cpu_baseline(args.cpu_reps) | host_cpu() | {"pinned_core": min(allowed)}
+        finally:
+            os.sched_setaffinity(0, allowed)
     print(json.dumps(rec), flush=True)
 
 
