@@ -145,3 +145,21 @@ def test_dispatch_weights_gather():
     assert (ew[p.pos[live]] == w[live]).all()
     untouched = np.setdiff1d(np.arange(cap), p.pos[live])
     assert (ew[untouched] == -1.0).all()
+
+
+@pytest.mark.parametrize("align,pad_empty", [(4, False), (16, True), (3, True)])
+def test_padding_keeps_the_true_counts(align, pad_empty):
+    """Padding moves rows, not counts: in_splits, src_offsets, out_splits and
+    expert_counts of a padded plan equal those of the plain plan; the padded
+    expert offsets are the exclusive scan of the padded sizes."""
+    rng = np.random.default_rng(40 + align)
+    T, K, E, W = 96, 4, 24, 4
+    ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    ids[ids % 7 == 3] = 5                       # some experts left empty
+    active = (rng.random(T) < 0.8).astype(np.uint8)
+    plain = oracle.plan(ids, E, W, active)
+    padded, _ = oracle.plan_ex(ids, E, W, active, major_align=align, pad_empty=pad_empty)
+    for f in ("in_splits", "src_offsets", "out_splits", "expert_counts"):
+        assert (getattr(padded, f) == getattr(plain, f)).all(), f
+    sizes = padded_rows(plain.expert_counts, align, pad_empty)
+    assert padded.expert_offsets.tolist() == (np.cumsum(sizes) - sizes).tolist()

@@ -104,3 +104,25 @@ def test_quant_combine_unit_and_power_of_two_scales(qtype):
     out4 = oracle.combine_quant(codes, qtype, fours, p.pos, inp.weights)
     ref4 = oracle.combine(workloads.bf16_bits_from_f32(dec * 4), p.pos, inp.weights)
     assert (out4 == ref4).all()
+
+
+@pytest.mark.parametrize("qtype", [1, 2])
+def test_quant_combine_uses_each_rows_own_scale(qtype):
+    """Per-row power-of-two scales (exact in bf16 with the decoded values):
+    the result equals the bf16 combine of decode(code) * scale[row], so a
+    scale taken from another row (the token's, or a neighbour's) fails."""
+    cfg, inp, p = case(seed=13)
+    rng = np.random.default_rng(2)
+    codes = rng.integers(0, 256, size=(cfg.cap_rows, cfg.H)).astype(np.uint8)
+    if qtype == 1:
+        codes[(codes & 0x7F) == 0x7F] = 0x10
+        dec = np.array([oracle.e4m3fn_decode(c) for c in range(256)], np.float32)[codes]
+    else:
+        codes[codes == 0x80] = 0
+        dec = codes.view(np.int8).astype(np.float32)
+    scales = (2.0 ** rng.integers(-6, 7, cfg.cap_rows)).astype(np.float32)
+    out = oracle.combine_quant(codes, qtype, scales, p.pos, inp.weights)
+    ref = oracle.combine(workloads.bf16_bits_from_f32(dec * scales[:, None]), p.pos, inp.weights)
+    assert (out == ref).all()
+    shifted = np.roll(scales, 1)
+    assert (oracle.combine_quant(codes, qtype, shifted, p.pos, inp.weights) != ref).any()
