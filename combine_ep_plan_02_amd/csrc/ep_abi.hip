@@ -565,13 +565,13 @@ void launch_tail(int V, dim3 grid, hipStream_t s, const ep::u32x4* y, const int3
   hipLaunchKernelGGL((ep::combine_add_rmsnorm_kernel<KMAX, NVV, NT, kCombineNtLoad, kCombineNtStore>), \
                      grid, dim3(NT), 0, s, y, pos, w, x, res, gamma, eps, ro, no, T, K, V, cap)
   if (nt == 256) {
-    if (NV <= 1) EP_TAIL(256, 1);
-    else EP_TAIL(256, 2);
+    EP_TAIL(256, 1);  // V <= 256
   } else if (nt == 512) {
-    EP_TAIL(512, 1);
+    EP_TAIL(512, 1);  // V <= 512
+  } else if (NV <= 1) {
+    EP_TAIL(1024, 1);
   } else {
-    if (NV <= 1) EP_TAIL(1024, 1);
-    else EP_TAIL(1024, 2);
+    EP_TAIL(1024, 2);  // V <= 2048 (H <= 16384)
   }
 #undef EP_TAIL
 }
