@@ -39,12 +39,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # the kernels built from the sources whose digest is `source_sha256`; any
 # other build reports traffic as null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "63a3c83f23e8f01ab32d17903c7af1c9a068d481e0c58189821a5de28d1207f4",
+    "source_sha256": "db10bc685a6b89c5d490fb55f9eb014e4181d8dcf1410f7ceb6b8b672cb6caf5",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "2": {"ep_plan": 1944444, "ep_dispatch": 1059731112, "ep_combine": 1061189362, "ep_dispatch_smooth": 876082137, "ep_combine_quant": 600762250, "ep_dispatch_int8": 590460090, "ep_combine_quant_int8": 600770634, "ep_combine_add_rmsnorm": 1294122011, "ep_add_rmsnorm": 469946107},
-        "4": {"ep_plan": 3565271, "ep_dispatch": 885915550, "ep_combine": 1652688803, "ep_dispatch_smooth": 2300942391, "ep_combine_quant": 969356912, "ep_dispatch_int8": 885965463, "ep_combine_quant_int8": 968719952, "ep_combine_add_rmsnorm": 2118411857, "ep_add_rmsnorm": 939702138},
-        "1": {"ep_plan": 651189, "ep_dispatch": 235766790, "ep_combine": 236503264, "ep_dispatch_smooth": 144420281, "ep_combine_quant": 138964789, "ep_dispatch_int8": 135604468, "ep_combine_quant_int8": 138717716},
-        "3": {"ep_all_to_all_splits": 268562925, "ep_plan_splits": 5920, "ep_dispatch_splits": 268574485},
+        "2": {"ep_plan": 1917953, "ep_dispatch": 1059643233, "ep_combine": 1061201145, "ep_dispatch_smooth": 875857257, "ep_combine_quant": 600735508, "ep_dispatch_int8": 590486245, "ep_combine_quant_int8": 600556340, "ep_combine_add_rmsnorm": 1294119486, "ep_add_rmsnorm": 469944903},
+        "4": {"ep_plan": 3544283, "ep_dispatch": 885923223, "ep_combine": 1652699353, "ep_dispatch_smooth": 2300574659, "ep_combine_quant": 969081338, "ep_dispatch_int8": 885995354, "ep_combine_quant_int8": 968602938, "ep_combine_add_rmsnorm": 2118404831, "ep_add_rmsnorm": 939700371},
+        "1": {"ep_plan": 642093, "ep_dispatch": 235733610, "ep_combine": 236514002, "ep_dispatch_smooth": 144415030, "ep_combine_quant": 138743971, "ep_dispatch_int8": 135594505, "ep_combine_quant_int8": 138662082},
+        "3": {"ep_all_to_all_splits": 268547134, "ep_plan_splits": 3872, "ep_dispatch_splits": 268562062},
     },
 }
 
