@@ -7,7 +7,9 @@
 //   pos = expert_offsets[e] + #(earlier live copies of expert e, all ranks)
 // which equals rank_offsets[d] + dst_offsets[s][e] + occurrence.
 //
-// Two kernels:
+// Two paths.  plan_fused_kernel (below) computes everything in one launch
+// when all tiles fit on the device at once: tiles exchange their counts as
+// self-validating descriptors while running.  Larger grids use two kernels:
 //  1. plan_tile_kernel -- one workgroup per tile of tokens of one source rank.
 //     Each wave ranks its 64-copy chunks in order with a ballot-based
 //     match-any over the expert-id bits (stable, no LDS atomics), keeping a
@@ -394,10 +396,10 @@ __global__ __launch_bounds__(kFinalizeThreads) void plan_finalize_kernel(
   }
 }
 
-
 // ---------------------------------------------------------------------------
-// Fused single-pass plan for grids whose tiles all fit on the device at once.  Each tile ranks its copies as in
-// plan_tile_kernel, then publishes its per-expert counts as 64-bit
+// Fused single-pass plan for grids whose tiles all fit on the device at
+// once.  Each tile ranks its copies as in plan_tile_kernel, then publishes
+// its per-expert counts as 64-bit
 // descriptors (call epoch << 32 | count) with relaxed device-scope atomic
 // stores: a descriptor carries its own validity, so no cache write-back or
 // invalidate is needed between publishing and reading.  Every tile then reads
