@@ -36,8 +36,9 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # HBM bytes per launch measured with rocprofv3 --pmc FETCH_SIZE and
 # WRITE_SIZE (KiB per dispatch; FETCH_SIZE scaled by 2.0 and WRITE_SIZE by
 # 1.0, the factors a plain 1 GiB copy gives), see profiles/.  They describe
-# the kernels built from the sources whose digest is `source_sha256`; any
-# other build reports traffic as null until the counters are taken again.
+# the kernels built from the sources whose digest is `source_sha256` (code
+# only, comments and whitespace aside); any other build reports traffic as
+# null until the counters are taken again.
 TRAFFIC = {
     "source_sha256": "db10bc685a6b89c5d490fb55f9eb014e4181d8dcf1410f7ceb6b8b672cb6caf5",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
@@ -50,13 +51,19 @@ TRAFFIC = {
 
 
 def source_digest() -> str:
+    """sha256 of the library's sources with comments and whitespace removed
+    (what the compiler sees), so a comment edit keeps the measured traffic."""
     import hashlib
+    import re
     d = os.path.join(ROOT, "combine_ep_plan_02_amd", "csrc")
     h = hashlib.sha256()
     for name in sorted(os.listdir(d)):
         if name.endswith((".h", ".hip")):
+            text = open(os.path.join(d, name), encoding="utf-8").read()
+            text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+            text = re.sub(r"//[^\n]*", " ", text)
             h.update(name.encode())
-            h.update(open(os.path.join(d, name), "rb").read())
+            h.update(" ".join(text.split()).encode())
     return h.hexdigest()
 
 
