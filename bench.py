@@ -40,12 +40,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # only, comments and whitespace aside); any other build reports traffic as
 # null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "db10bc685a6b89c5d490fb55f9eb014e4181d8dcf1410f7ceb6b8b672cb6caf5",
+    "source_sha256": "7d37dc1e9494aa8f4433f32a53eac5527d53f466ee0e86f1978e04203a9e795f",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "2": {"ep_plan": 1917953, "ep_dispatch": 1059643233, "ep_combine": 1061201145, "ep_dispatch_smooth": 875857257, "ep_combine_quant": 600735508, "ep_dispatch_int8": 590486245, "ep_combine_quant_int8": 600556340, "ep_combine_add_rmsnorm": 1294119486, "ep_add_rmsnorm": 469944903},
-        "4": {"ep_plan": 3544283, "ep_dispatch": 885923223, "ep_combine": 1652699353, "ep_dispatch_smooth": 2300574659, "ep_combine_quant": 969081338, "ep_dispatch_int8": 885995354, "ep_combine_quant_int8": 968602938, "ep_combine_add_rmsnorm": 2118404831, "ep_add_rmsnorm": 939700371},
-        "1": {"ep_plan": 642093, "ep_dispatch": 235733610, "ep_combine": 236514002, "ep_dispatch_smooth": 144415030, "ep_combine_quant": 138743971, "ep_dispatch_int8": 135594505, "ep_combine_quant_int8": 138662082},
-        "3": {"ep_all_to_all_splits": 268547134, "ep_plan_splits": 3872, "ep_dispatch_splits": 268562062},
+        "2": {"ep_plan": 1923977, "ep_dispatch": 1059717051, "ep_combine": 1061201097, "ep_dispatch_smooth": 875730076, "ep_combine_quant": 600629435, "ep_dispatch_int8": 590503063, "ep_combine_quant_int8": 600435707, "ep_combine_add_rmsnorm": 1294119352, "ep_add_rmsnorm": 469944971},
+        "4": {"ep_plan": 3545011, "ep_dispatch": 885909911, "ep_combine": 1652699184, "ep_dispatch_smooth": 2301813043, "ep_combine_quant": 969397285, "ep_dispatch_int8": 885973821, "ep_combine_quant_int8": 968559621, "ep_combine_add_rmsnorm": 2118404578, "ep_add_rmsnorm": 939700411},
+        "1": {"ep_plan": 640741, "ep_dispatch": 235761742, "ep_combine": 236513970, "ep_dispatch_smooth": 144415057, "ep_combine_quant": 138707510, "ep_dispatch_int8": 135616237, "ep_combine_quant_int8": 138597910},
+        "3": {"ep_all_to_all_splits": 268546406, "ep_plan_splits": 3872, "ep_dispatch_splits": 268566942},
     },
 }
 
