@@ -79,6 +79,21 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// Rows of a [cap_rows][...] buffer that a kernel can reach: positions are
+// int32, so rows at or past 2^31 are never read or written.  Byte ranges for
+// the overlap checks are taken over these rows, which keeps them from
+// overflowing for any cap_rows.
+size_t reachable_rows(int64_t cap_rows) {
+  const int64_t lim = (int64_t)1 << 31;
+  return (size_t)(cap_rows < lim ? cap_rows : lim);
+}
+
+// W * R * stride_bytes (the bytes of the all-to-all's in and out buffers)
+// fits in int64.
+bool splits_bytes_fit(int32_t W, int64_t R, int64_t stride_bytes) {
+  return R == 0 || R <= INT64_MAX / W / stride_bytes;
+}
+
 int launch_status(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(EP_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
@@ -336,14 +351,15 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
   if (!aligned(weights, 4) || !aligned(expand_weights, 4))
     return fail(EP_ERR_INVALID, "weights and expand_weights must be 4-byte aligned");
   const size_t xb = (size_t)T * H * 2, pb = (size_t)T * K * 4;
-  const size_t eb = (size_t)cap_rows * H * (quant ? 1 : 2);
-  const size_t sb = quant ? (size_t)cap_rows * 4 : 0;
+  const size_t cap = reachable_rows(cap_rows);
+  const size_t eb = cap * H * (quant ? 1 : 2);
+  const size_t sb = quant ? cap * 4 : 0;
   if (overlap(expand_x, eb, x, xb) || overlap(expand_x, eb, pos, pb))
     return fail(EP_ERR_INVALID, "expand_x overlaps an input");
   if (quant && (overlap(expand_scales, sb, x, xb) || overlap(expand_scales, sb, pos, pb) ||
               overlap(expand_scales, sb, expand_x, eb)))
     return fail(EP_ERR_INVALID, "expand_scales overlaps another buffer");
-  const size_t wb = expand_weights ? (size_t)cap_rows * 4 : 0;
+  const size_t wb = expand_weights ? cap * 4 : 0;
   if (expand_weights &&
       (overlap(expand_weights, wb, x, xb) || overlap(expand_weights, wb, pos, pb) ||
        overlap(expand_weights, wb, expand_x, eb) || overlap(expand_weights, wb, weights, pb) ||
@@ -398,7 +414,7 @@ EP_EXPORT int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t* y, int
   if (!aligned(y, 16) || !aligned(out, 16)) return fail(EP_ERR_INVALID, "y and out must be 16-byte aligned");
   if (!aligned(pos, 4) || !aligned(weights, 4)) return fail(EP_ERR_INVALID, "pos and weights must be 4-byte aligned");
   const size_t ob = (size_t)T * H * 2;
-  if (overlap(out, ob, y, (size_t)cap_rows * H * 2) || overlap(out, ob, pos, (size_t)T * K * 4) ||
+  if (overlap(out, ob, y, reachable_rows(cap_rows) * H * 2) || overlap(out, ob, pos, (size_t)T * K * 4) ||
       overlap(out, ob, weights, (size_t)T * K * 4))
     return fail(EP_ERR_INVALID, "out overlaps an input");
 
@@ -448,7 +464,7 @@ EP_EXPORT int ep_dispatch_smooth(int32_t T, int32_t K, int32_t E, int32_t H, con
     return fail(EP_ERR_INVALID, "x, expand_x and smooth_scales must be 16-byte aligned");
   if (!aligned(topk_ids, 4) || !aligned(pos, 4) || !aligned(expand_scales, 4))
     return fail(EP_ERR_INVALID, "topk_ids, pos and expand_scales must be 4-byte aligned");
-  const size_t eb = (size_t)cap_rows * H, sb = (size_t)cap_rows * 4;
+  const size_t eb = reachable_rows(cap_rows) * H, sb = reachable_rows(cap_rows) * 4;
   const Range_ ins[] = {{x, (size_t)T * H * 2}, {topk_ids, (size_t)T * K * 4}, {pos, (size_t)T * K * 4},
                         {smooth_scales, (size_t)E * H * 4}};
   for (const auto& r : ins)
@@ -494,7 +510,8 @@ EP_EXPORT int ep_combine_quant(int32_t T, int32_t K, int32_t H, const void* code
   if (!aligned(row_scales, 4) || !aligned(pos, 4) || !aligned(weights, 4))
     return fail(EP_ERR_INVALID, "row_scales, pos and weights must be 4-byte aligned");
   const size_t ob = (size_t)T * H * 2;
-  if (overlap(out, ob, codes, (size_t)cap_rows * H) || overlap(out, ob, row_scales, (size_t)cap_rows * 4) ||
+  if (overlap(out, ob, codes, reachable_rows(cap_rows) * H) ||
+      overlap(out, ob, row_scales, reachable_rows(cap_rows) * 4) ||
       overlap(out, ob, pos, (size_t)T * K * 4) || overlap(out, ob, weights, (size_t)T * K * 4))
     return fail(EP_ERR_INVALID, "out overlaps an input");
   const int NG = H / 16;
@@ -591,7 +608,7 @@ EP_EXPORT int ep_combine_add_rmsnorm(int32_t T, int32_t K, int32_t H, const uint
   if (!y || !pos || !weights) return fail(EP_ERR_NULLPTR, "y, pos and weights are required");
   if (!aligned(y, 16)) return fail(EP_ERR_INVALID, "y must be 16-byte aligned");
   if (!aligned(pos, 4) || !aligned(weights, 4)) return fail(EP_ERR_INVALID, "pos and weights must be 4-byte aligned");
-  const size_t rb = (size_t)T * H * 2, yb = (size_t)cap_rows * H * 2, pb = (size_t)T * K * 4;
+  const size_t rb = (size_t)T * H * 2, yb = reachable_rows(cap_rows) * H * 2, pb = (size_t)T * K * 4;
   for (const void* o : {(const void*)residual_out, (const void*)norm_out})
     if (overlap(o, rb, y, yb) || overlap(o, rb, pos, pb) || overlap(o, rb, weights, pb))
       return fail(EP_ERR_INVALID, "an output overlaps an input");
@@ -657,6 +674,8 @@ EP_EXPORT int ep_dispatch_splits(int32_t W, int64_t R, int64_t stride_bytes, con
   if (stride_bytes <= 0 || stride_bytes % 16)
     return fail(EP_ERR_UNSUPPORTED, "stride_bytes must be a positive multiple of 16 (got %lld)",
                 (long long)stride_bytes);
+  if (!splits_bytes_fit(W, R, stride_bytes))
+    return fail(EP_ERR_UNSUPPORTED, "W * R * stride_bytes must fit in 63 bits");
   if (R == 0) return ok();
   if (!in || !out || !src_offsets || !out_splits || !dst_offsets || !rank_offsets)
     return fail(EP_ERR_NULLPTR, "all buffers are required");
@@ -705,6 +724,8 @@ EP_EXPORT int ep_all_to_all_splits(int32_t W, int64_t R, int64_t stride_bytes, c
   if (stride_bytes <= 0 || stride_bytes % 16)
     return fail(EP_ERR_UNSUPPORTED, "stride_bytes must be a positive multiple of 16 (got %lld)",
                 (long long)stride_bytes);
+  if (!splits_bytes_fit(W, R, stride_bytes))
+    return fail(EP_ERR_UNSUPPORTED, "W * R * stride_bytes must fit in 63 bits");
   const bool any_plan = src_offsets || out_splits || dst_offsets || rank_offsets;
   if (R == 0 && !any_plan) return ok();
   if (!in_splits) return fail(EP_ERR_NULLPTR, "in_splits is required");

@@ -287,8 +287,9 @@ int ep_plan_splits(int32_t W, const int64_t *in_splits, int64_t *src_offsets,
  *   in[p][src_offsets[r][p] + i]  ->  out[rank_offsets[r] + dst_offsets[r][p] + i]
  * for i < out_splits[r][p].  in [W][R] rows, out [W*R] rows (the packed
  * receive buffers of all ranks), each row `stride_bytes` long (multiple of
- * 16; in, out 16-byte aligned).  A chunk that would read past row R of its
- * sender or write past row W*R is skipped and sets EP_DEVERR_SPLITS. */
+ * 16; in, out 16-byte aligned; W*R*stride_bytes < 2^63, else
+ * EP_ERR_UNSUPPORTED).  A chunk that would read past row R of its sender or
+ * write past row W*R is skipped and sets EP_DEVERR_SPLITS. */
 int ep_dispatch_splits(int32_t W, int64_t R, int64_t stride_bytes, const void *in,
                        const int64_t *src_offsets, const int64_t *out_splits,
                        const int64_t *dst_offsets, const int64_t *rank_offsets, void *out,
@@ -302,7 +303,8 @@ int ep_dispatch_splits(int32_t W, int64_t R, int64_t stride_bytes, const void *i
  * rank_offsets ([W+1]), each of which may be NULL (not written).  A chunk
  * whose rows fall outside the buffers is skipped and sets
  * EP_DEVERR_SPLITS.  R == 0 with no plan output requested enqueues
- * nothing; in and out may be NULL when R == 0. */
+ * nothing; in and out may be NULL when R == 0.  Same row and size limits
+ * as ep_dispatch_splits. */
 int ep_all_to_all_splits(int32_t W, int64_t R, int64_t stride_bytes, const int64_t *in_splits,
                          const void *in, void *out, int64_t *src_offsets, int64_t *out_splits,
                          int64_t *dst_offsets, int64_t *rank_offsets, void *stream);

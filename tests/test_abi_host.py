@@ -267,3 +267,36 @@ def test_fused_splits_rejections(ep):
     assert f(8, 16, 32, S, I, O, P1, P1 + 8, None, None, None) == ep.EP_ERR_INVALID    # plan arrays overlap
     assert f(8, 16, 32, S, I, O, S, None, None, None, None) == ep.EP_ERR_INVALID       # plan over in_splits
     assert f(8, 0, 32, None, None, None, None, None, None, None, None) == ep.EP_OK     # nothing to do
+
+
+def test_huge_capacity_keeps_overlap_checks(ep):
+    # A capacity far beyond what int32 positions can reach: the byte range
+    # cap_rows * H * 2 would wrap around 2^64 (here to 0), so the overlap
+    # checks take the rows a position can reach (< 2^31) instead.  An output
+    # inside y's first rows is still an overlap, for every combine and dispatch.
+    huge = 1 << 62
+    Y, P, Wt, X = A, A + (1 << 34), A + (1 << 35), A + (1 << 36)
+    inside = Y + 1024
+    assert ep.lib.ep_combine(64, 2, 8, Y, huge, P, Wt, inside, None) == ep.EP_ERR_INVALID
+    assert "overlaps" in ep.lib.ep_last_error().decode()
+    F8 = ep.EP_FP8_E4M3FN
+    assert ep.lib.ep_combine_quant(64, 2, 16, Y, F8, X, huge, P, Wt, inside, None) == ep.EP_ERR_INVALID
+    assert ep.lib.ep_combine_add_rmsnorm(64, 2, 8, Y, huge, P, Wt, X, X + 4096, 1e-6,
+                                         inside, X + (1 << 20), None) == ep.EP_ERR_INVALID
+    # dispatch: expand_x over x, x placed inside expand_x's reachable rows
+    assert ep.lib.ep_dispatch(64, 2, 8, inside, P, ep.EP_BF16, Y, None, None, None, huge,
+                              None) == ep.EP_ERR_INVALID
+
+
+def test_splits_size_overflow_is_rejected(ep):
+    # W * R * stride_bytes beyond int64: refused before any byte range is formed
+    B = [A + i * (1 << 30) for i in range(5)]
+    IN, OUT = A + (1 << 36), A + (1 << 37)
+    R = (1 << 62) // 16
+    assert ep.lib.ep_dispatch_splits(8, R, 32, IN, *B[1:], OUT, None) == ep.EP_ERR_UNSUPPORTED
+    assert "63 bits" in ep.lib.ep_last_error().decode()
+    assert ep.lib.ep_all_to_all_splits(8, R, 32, B[0], IN, OUT, None, None, None, None,
+                                       None) == ep.EP_ERR_UNSUPPORTED
+    # the largest R whose buffers fit still passes this check (and fails later on the aliasing)
+    R_fit = ((1 << 63) - 1) // 8 // 32
+    assert ep.lib.ep_dispatch_splits(8, R_fit, 32, IN, *B[1:], IN, None) == ep.EP_ERR_INVALID
