@@ -40,12 +40,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # only, comments and whitespace aside); any other build reports traffic as
 # null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "7d37dc1e9494aa8f4433f32a53eac5527d53f466ee0e86f1978e04203a9e795f",
+    "source_sha256": "b5e1ba99e6fd415f0c441854ab45c6644d1884ac298792a827533919612cbdd9",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "2": {"ep_plan": 1923977, "ep_dispatch": 1059717051, "ep_combine": 1061201097, "ep_dispatch_smooth": 875730076, "ep_combine_quant": 600629435, "ep_dispatch_int8": 590503063, "ep_combine_quant_int8": 600435707, "ep_combine_add_rmsnorm": 1294119352, "ep_add_rmsnorm": 469944971},
-        "4": {"ep_plan": 3545011, "ep_dispatch": 885909911, "ep_combine": 1652699184, "ep_dispatch_smooth": 2301813043, "ep_combine_quant": 969397285, "ep_dispatch_int8": 885973821, "ep_combine_quant_int8": 968559621, "ep_combine_add_rmsnorm": 2118404578, "ep_add_rmsnorm": 939700411},
-        "1": {"ep_plan": 640741, "ep_dispatch": 235761742, "ep_combine": 236513970, "ep_dispatch_smooth": 144415057, "ep_combine_quant": 138707510, "ep_dispatch_int8": 135616237, "ep_combine_quant_int8": 138597910},
-        "3": {"ep_all_to_all_splits": 268546406, "ep_plan_splits": 3872, "ep_dispatch_splits": 268566942},
+        "1": {"ep_plan": 640621, "ep_dispatch": 235753173, "ep_combine": 236513952, "ep_dispatch_smooth": 144415639, "ep_combine_quant": 138726257, "ep_dispatch_int8": 135610196, "ep_combine_quant_int8": 138656945},
+        "2": {"ep_plan": 1922241, "ep_dispatch": 1059665934, "ep_combine": 1061201052, "ep_dispatch_smooth": 876050144, "ep_combine_quant": 600829029, "ep_dispatch_int8": 590488129, "ep_combine_quant_int8": 600714212, "ep_combine_add_rmsnorm": 1294119270, "ep_add_rmsnorm": 469944864},
+        "3": {"ep_all_to_all_splits": 268552624, "ep_plan_splits": 3872, "ep_dispatch_splits": 268563768},
+        "4": {"ep_plan": 3545098, "ep_dispatch": 885897025, "ep_combine": 1652699116, "ep_dispatch_smooth": 2300720158, "ep_combine_quant": 968297987, "ep_dispatch_int8": 885940828, "ep_combine_quant_int8": 968334403, "ep_combine_add_rmsnorm": 2118406075, "ep_add_rmsnorm": 939700325},
     },
 }
 
