@@ -94,6 +94,17 @@ bool splits_bytes_fit(int32_t W, int64_t R, int64_t stride_bytes) {
   return R == 0 || R <= INT64_MAX / W / stride_bytes;
 }
 
+// Tokens one launch of a row kernel covers.  A launch holds at most
+// 2^32 - 1 work-items per grid dimension; the row kernels' grids grow with
+// the token count, so the host launches them over slices of at most 2^31
+// work-items, offsetting the per-token pointers (x, pos, weights, out, ...)
+// by the slice's first token.  Rows addressed through pos are global and
+// need no offset.  Every workload of practical size is one slice.
+int64_t slice_tokens(int64_t work_items_per_token) {
+  const int64_t n = ((int64_t)1 << 31) / work_items_per_token;
+  return n > 0 ? n : 1;
+}
+
 int launch_status(const char* what) {
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(EP_ERR_HIP, "%s: launch failed: %s", what, hipGetErrorString(e));
@@ -371,34 +382,46 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
   if (!quant) {
     const int V = H / 8;
     const int chunks = (V + ep::kWave * kDispatchUnroll - 1) / (ep::kWave * kDispatchUnroll);
-    const int64_t items = (int64_t)T * chunks;
-    if ((items + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock > INT32_MAX)
-      return fail(EP_ERR_UNSUPPORTED, "T * H too large for one launch");
-    const dim3 cgrid((unsigned)((items + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock));
-    hipLaunchKernelGGL((ep::dispatch_bf16_kernel<kDispatchUnroll, kDispatchNtLoad, kDispatchNtStore>), cgrid,
-                       block, 0, s, (const ep::u32x4*)x, pos, (ep::u32x4*)expand_x, weights, expand_weights, T, K,
-                       V, chunks, cap_rows);
-    return launch_status("ep_dispatch (bf16)");
+    const int64_t Ts = slice_tokens((int64_t)chunks * ep::kWave);
+    for (int64_t t0 = 0; t0 < T; t0 += Ts) {
+      const int Tn = (int)(T - t0 < Ts ? T - t0 : Ts);
+      const int64_t items = (int64_t)Tn * chunks;
+      const dim3 cgrid((unsigned)((items + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock));
+      hipLaunchKernelGGL((ep::dispatch_bf16_kernel<kDispatchUnroll, kDispatchNtLoad, kDispatchNtStore>), cgrid,
+                         block, 0, s, (const ep::u32x4*)x + t0 * V, pos + t0 * K, (ep::u32x4*)expand_x,
+                         weights ? weights + t0 * K : nullptr, expand_weights, Tn, K, V, chunks, cap_rows);
+      rc = launch_status("ep_dispatch (bf16)");
+      if (rc) return rc;
+    }
+    return ok();
   }
   const int NG = H / 16;
-  const ep::u32x4* xv = (const ep::u32x4*)x;
   ep::u32x4* qv = (ep::u32x4*)expand_x;
-  const dim3 tgrid((unsigned)T);  // one workgroup per token
   const int per_thread = (NG + ep::kRowThreads - 1) / ep::kRowThreads;
-  auto launch = [&](auto qt) {
-    constexpr int QT = decltype(qt)::value;
+  const int64_t Ts = slice_tokens(ep::kRowThreads);  // one workgroup per token
+  for (int64_t t0 = 0; t0 < T; t0 += Ts) {
+    const int Tn = (int)(T - t0 < Ts ? T - t0 : Ts);
+    const dim3 tgrid((unsigned)Tn);
+    const ep::u32x4* xv = (const ep::u32x4*)x + t0 * NG * 2;
+    const int32_t* pn = pos + t0 * K;
+    const float* wn = weights ? weights + t0 * K : nullptr;
+    auto launch = [&](auto qt) {
+      constexpr int QT = decltype(qt)::value;
 #define EP_QDISP(G)                                                                                          \
-  hipLaunchKernelGGL((ep::dispatch_quant_kernel<QT, G, kQuantNtLoad, kQuantNtStore>), tgrid, block, 0, s, xv, pos, qv, \
-                     expand_scales, weights, expand_weights, T, K, NG, cap_rows)
-    if (per_thread <= 1) EP_QDISP(1);
-    else if (per_thread <= 2) EP_QDISP(2);
-    else if (per_thread <= 4) EP_QDISP(4);
-    else EP_QDISP(8);
+  hipLaunchKernelGGL((ep::dispatch_quant_kernel<QT, G, kQuantNtLoad, kQuantNtStore>), tgrid, block, 0, s, xv, pn, qv, \
+                     expand_scales, wn, expand_weights, Tn, K, NG, cap_rows)
+      if (per_thread <= 1) EP_QDISP(1);
+      else if (per_thread <= 2) EP_QDISP(2);
+      else if (per_thread <= 4) EP_QDISP(4);
+      else EP_QDISP(8);
 #undef EP_QDISP
-  };
-  if (out_dtype == EP_FP8_E4M3FN) launch(std::integral_constant<int, ep::kQFp8>{});
-  else launch(std::integral_constant<int, ep::kQInt8>{});
-  return launch_status("ep_dispatch (quantised rows)");
+    };
+    if (out_dtype == EP_FP8_E4M3FN) launch(std::integral_constant<int, ep::kQFp8>{});
+    else launch(std::integral_constant<int, ep::kQInt8>{});
+    rc = launch_status("ep_dispatch (quantised rows)");
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 EP_EXPORT int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t* y, int64_t cap_rows,
@@ -422,22 +445,28 @@ EP_EXPORT int ep_combine(int32_t T, int32_t K, int32_t H, const uint16_t* y, int
   const dim3 block(kCombineWaves * ep::kWave);
   const int V = H / 8;
   const int chunks = (V + ep::kWave * kCombineUnroll - 1) / (ep::kWave * kCombineUnroll);
-  const int64_t items = (int64_t)T * chunks;
-  if ((items + kCombineWaves - 1) / kCombineWaves > INT32_MAX)
-    return fail(EP_ERR_UNSUPPORTED, "T * H too large for one launch");
-  const dim3 cgrid((unsigned)((items + kCombineWaves - 1) / kCombineWaves));
   const ep::u32x4* yv = (const ep::u32x4*)y;
-  ep::u32x4* ov = (ep::u32x4*)out;
-  if (K <= 4)
-    hipLaunchKernelGGL((ep::combine_kernel<4, kCombineUnroll, kCombineWaves, kCombineNtLoad, kCombineNtStore>),
-                       cgrid, block, 0, s, yv, pos, weights, ov, T, K, V, chunks, cap_rows);
-  else if (K <= 8)
-    hipLaunchKernelGGL((ep::combine_kernel<8, kCombineUnroll, kCombineWaves, kCombineNtLoad, kCombineNtStore>),
-                       cgrid, block, 0, s, yv, pos, weights, ov, T, K, V, chunks, cap_rows);
-  else
-    hipLaunchKernelGGL((ep::combine_kernel<16, kCombineUnroll, kCombineWaves, kCombineNtLoad, kCombineNtStore>),
-                       cgrid, block, 0, s, yv, pos, weights, ov, T, K, V, chunks, cap_rows);
-  return launch_status("ep_combine");
+  const int64_t Ts = slice_tokens((int64_t)chunks * ep::kWave);
+  for (int64_t t0 = 0; t0 < T; t0 += Ts) {
+    const int Tn = (int)(T - t0 < Ts ? T - t0 : Ts);
+    const int64_t items = (int64_t)Tn * chunks;
+    const dim3 cgrid((unsigned)((items + kCombineWaves - 1) / kCombineWaves));
+    const int32_t* pn = pos + t0 * K;
+    const float* wn = weights + t0 * K;
+    ep::u32x4* ov = (ep::u32x4*)out + t0 * V;
+    if (K <= 4)
+      hipLaunchKernelGGL((ep::combine_kernel<4, kCombineUnroll, kCombineWaves, kCombineNtLoad, kCombineNtStore>),
+                         cgrid, block, 0, s, yv, pn, wn, ov, Tn, K, V, chunks, cap_rows);
+    else if (K <= 8)
+      hipLaunchKernelGGL((ep::combine_kernel<8, kCombineUnroll, kCombineWaves, kCombineNtLoad, kCombineNtStore>),
+                         cgrid, block, 0, s, yv, pn, wn, ov, Tn, K, V, chunks, cap_rows);
+    else
+      hipLaunchKernelGGL((ep::combine_kernel<16, kCombineUnroll, kCombineWaves, kCombineNtLoad, kCombineNtStore>),
+                         cgrid, block, 0, s, yv, pn, wn, ov, Tn, K, V, chunks, cap_rows);
+    rc = launch_status("ep_combine");
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 constexpr int kSmoothMaxH = 16384;  // 4 groups of 16 values per thread stay in VGPRs
@@ -474,22 +503,30 @@ EP_EXPORT int ep_dispatch_smooth(int32_t T, int32_t K, int32_t E, int32_t H, con
   const int NG = H / 16;
   const int per_thread = (NG + ep::kRowThreads - 1) / ep::kRowThreads;
   hipStream_t s = (hipStream_t)stream;
-  const ep::u32x4* xv = (const ep::u32x4*)x;
   const float4* sm = (const float4*)smooth_scales;
   ep::u32x4* qv = (ep::u32x4*)expand_x;
-  auto launch = [&](auto qt) {
-    constexpr int QT = decltype(qt)::value;
+  const int64_t Ts = slice_tokens(ep::kRowThreads);  // one workgroup per token
+  for (int64_t t0 = 0; t0 < T; t0 += Ts) {
+    const int Tn = (int)(T - t0 < Ts ? T - t0 : Ts);
+    const ep::u32x4* xv = (const ep::u32x4*)x + t0 * NG * 2;
+    const int32_t* idn = topk_ids + t0 * K;
+    const int32_t* pn = pos + t0 * K;
+    auto launch = [&](auto qt) {
+      constexpr int QT = decltype(qt)::value;
 #define EP_SMOOTH(G)                                                                                      \
-  hipLaunchKernelGGL((ep::dispatch_smooth_kernel<QT, G, kQuantNtStore>), dim3((unsigned)T), dim3(ep::kRowThreads), \
-                     0, s, xv, topk_ids, pos, sm, qv, expand_scales, T, K, E, NG, cap_rows)
-    if (per_thread <= 1) EP_SMOOTH(1);
-    else if (per_thread <= 2) EP_SMOOTH(2);
-    else EP_SMOOTH(4);
+  hipLaunchKernelGGL((ep::dispatch_smooth_kernel<QT, G, kQuantNtStore>), dim3((unsigned)Tn), dim3(ep::kRowThreads), \
+                     0, s, xv, idn, pn, sm, qv, expand_scales, Tn, K, E, NG, cap_rows)
+      if (per_thread <= 1) EP_SMOOTH(1);
+      else if (per_thread <= 2) EP_SMOOTH(2);
+      else EP_SMOOTH(4);
 #undef EP_SMOOTH
-  };
-  if (out_dtype == EP_FP8_E4M3FN) launch(std::integral_constant<int, ep::kQFp8>{});
-  else launch(std::integral_constant<int, ep::kQInt8>{});
-  return launch_status("ep_dispatch_smooth");
+    };
+    if (out_dtype == EP_FP8_E4M3FN) launch(std::integral_constant<int, ep::kQFp8>{});
+    else launch(std::integral_constant<int, ep::kQInt8>{});
+    rc = launch_status("ep_dispatch_smooth");
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 EP_EXPORT int ep_combine_quant(int32_t T, int32_t K, int32_t H, const void* codes, int32_t code_dtype,
@@ -516,29 +553,35 @@ EP_EXPORT int ep_combine_quant(int32_t T, int32_t K, int32_t H, const void* code
     return fail(EP_ERR_INVALID, "out overlaps an input");
   const int NG = H / 16;
   const int chunks = (NG + ep::kWave - 1) / ep::kWave;
-  const int64_t items = (int64_t)T * chunks;
-  if ((items + kCombineQuantWaves - 1) / kCombineQuantWaves > INT32_MAX)
-    return fail(EP_ERR_UNSUPPORTED, "T * H too large for one launch");
-  const dim3 grid((unsigned)((items + kCombineQuantWaves - 1) / kCombineQuantWaves));
   const dim3 block(kCombineQuantWaves * ep::kWave);
   hipStream_t s = (hipStream_t)stream;
   const ep::u32x4* cv = (const ep::u32x4*)codes;
-  ep::u32x4* ov = (ep::u32x4*)out;
-  auto launch = [&](auto qt) {
-    constexpr int QT = decltype(qt)::value;
-    if (K <= 4)
-      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 4, kCombineQuantWaves, kCombineNtLoad, kCombineNtStore>), grid,
-                         block, 0, s, cv, row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
-    else if (K <= 8)
-      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 8, kCombineQuantWaves, kCombineNtLoad, kCombineNtStore>), grid,
-                         block, 0, s, cv, row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
-    else
-      hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 16, kCombineQuantWaves, kCombineNtLoad, kCombineNtStore>), grid,
-                         block, 0, s, cv, row_scales, pos, weights, ov, T, K, NG, chunks, cap_rows);
-  };
-  if (code_dtype == EP_FP8_E4M3FN) launch(std::integral_constant<int, ep::kQFp8>{});
-  else launch(std::integral_constant<int, ep::kQInt8>{});
-  return launch_status("ep_combine_quant");
+  const int64_t Ts = slice_tokens((int64_t)chunks * ep::kWave);
+  for (int64_t t0 = 0; t0 < T; t0 += Ts) {
+    const int Tn = (int)(T - t0 < Ts ? T - t0 : Ts);
+    const int64_t items = (int64_t)Tn * chunks;
+    const dim3 grid((unsigned)((items + kCombineQuantWaves - 1) / kCombineQuantWaves));
+    const int32_t* pn = pos + t0 * K;
+    const float* wn = weights + t0 * K;
+    ep::u32x4* ov = (ep::u32x4*)out + t0 * NG * 2;
+    auto launch = [&](auto qt) {
+      constexpr int QT = decltype(qt)::value;
+      if (K <= 4)
+        hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 4, kCombineQuantWaves, kCombineNtLoad, kCombineNtStore>),
+                           grid, block, 0, s, cv, row_scales, pn, wn, ov, Tn, K, NG, chunks, cap_rows);
+      else if (K <= 8)
+        hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 8, kCombineQuantWaves, kCombineNtLoad, kCombineNtStore>),
+                           grid, block, 0, s, cv, row_scales, pn, wn, ov, Tn, K, NG, chunks, cap_rows);
+      else
+        hipLaunchKernelGGL((ep::combine_quant_kernel<QT, 16, kCombineQuantWaves, kCombineNtLoad, kCombineNtStore>),
+                           grid, block, 0, s, cv, row_scales, pn, wn, ov, Tn, K, NG, chunks, cap_rows);
+    };
+    if (code_dtype == EP_FP8_E4M3FN) launch(std::integral_constant<int, ep::kQFp8>{});
+    else launch(std::integral_constant<int, ep::kQInt8>{});
+    rc = launch_status("ep_combine_quant");
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 namespace {
@@ -572,25 +615,41 @@ int check_tail(int32_t T, int32_t H, const void* residual, const void* gamma, fl
 // the same order and their outputs are bit-identical.
 int tail_threads(int V) { return V <= 256 ? 256 : V <= 512 ? 512 : 1024; }
 
+// One workgroup per token, launched over token slices (slice_tokens); x and
+// pos / w are NULL for the tail alone and for no combine input respectively.
 template <int KMAX>
-void launch_tail(int V, dim3 grid, hipStream_t s, const ep::u32x4* y, const int32_t* pos, const float* w,
-                 const ep::u32x4* x, const ep::u32x4* res, const ep::u32x4* gamma, float eps, ep::u32x4* ro,
-                 ep::u32x4* no, int T, int K, int64_t cap) {
+int launch_tail(const char* what, int V, hipStream_t s, const ep::u32x4* y, const int32_t* pos,
+                const float* w, const ep::u32x4* x, const ep::u32x4* res, const ep::u32x4* gamma, float eps,
+                ep::u32x4* ro, ep::u32x4* no, int T, int K, int64_t cap) {
   const int nt = tail_threads(V);
   const int NV = (V + nt - 1) / nt;
+  const int64_t Ts = slice_tokens(nt);
+  for (int64_t t0 = 0; t0 < T; t0 += Ts) {
+    const int Tn = (int)(T - t0 < Ts ? T - t0 : Ts);
+    const dim3 grid((unsigned)Tn);
+    const int32_t* pn = pos ? pos + t0 * K : nullptr;
+    const float* wn = w ? w + t0 * K : nullptr;
+    const ep::u32x4* xn = x ? x + t0 * V : nullptr;
+    const ep::u32x4* rn = res + t0 * V;
+    ep::u32x4* ron = ro + t0 * V;
+    ep::u32x4* non = no + t0 * V;
 #define EP_TAIL(NT, NVV)                                                                            \
   hipLaunchKernelGGL((ep::combine_add_rmsnorm_kernel<KMAX, NVV, NT, kCombineNtLoad, kCombineNtStore>), \
-                     grid, dim3(NT), 0, s, y, pos, w, x, res, gamma, eps, ro, no, T, K, V, cap)
-  if (nt == 256) {
-    EP_TAIL(256, 1);  // V <= 256
-  } else if (nt == 512) {
-    EP_TAIL(512, 1);  // V <= 512
-  } else if (NV <= 1) {
-    EP_TAIL(1024, 1);
-  } else {
-    EP_TAIL(1024, 2);  // V <= 2048 (H <= 16384)
-  }
+                     grid, dim3(NT), 0, s, y, pn, wn, xn, rn, gamma, eps, ron, non, Tn, K, V, cap)
+    if (nt == 256) {
+      EP_TAIL(256, 1);  // V <= 256
+    } else if (nt == 512) {
+      EP_TAIL(512, 1);  // V <= 512
+    } else if (NV <= 1) {
+      EP_TAIL(1024, 1);
+    } else {
+      EP_TAIL(1024, 2);  // V <= 2048 (H <= 16384)
+    }
 #undef EP_TAIL
+    const int rc = launch_status(what);
+    if (rc) return rc;
+  }
+  return ok();
 }
 
 }  // namespace
@@ -614,16 +673,14 @@ EP_EXPORT int ep_combine_add_rmsnorm(int32_t T, int32_t K, int32_t H, const uint
       return fail(EP_ERR_INVALID, "an output overlaps an input");
   const int V = H / 8;
   hipStream_t s = (hipStream_t)stream;
-  const dim3 grid((unsigned)T);
   auto args = [&](auto launch) {
-    launch(V, grid, s, (const ep::u32x4*)y, pos, weights, (const ep::u32x4*)nullptr,
-           (const ep::u32x4*)residual, (const ep::u32x4*)gamma, eps, (ep::u32x4*)residual_out,
-           (ep::u32x4*)norm_out, T, K, cap_rows);
+    return launch("ep_combine_add_rmsnorm", V, s, (const ep::u32x4*)y, pos, weights,
+                  (const ep::u32x4*)nullptr, (const ep::u32x4*)residual, (const ep::u32x4*)gamma, eps,
+                  (ep::u32x4*)residual_out, (ep::u32x4*)norm_out, T, K, cap_rows);
   };
-  if (K <= 4) args(launch_tail<4>);
-  else if (K <= 8) args(launch_tail<8>);
-  else args(launch_tail<16>);
-  return launch_status("ep_combine_add_rmsnorm");
+  if (K <= 4) return args(launch_tail<4>);
+  if (K <= 8) return args(launch_tail<8>);
+  return args(launch_tail<16>);
 }
 
 EP_EXPORT int ep_add_rmsnorm(int32_t T, int32_t H, const uint16_t* x, const uint16_t* residual,
@@ -638,10 +695,9 @@ EP_EXPORT int ep_add_rmsnorm(int32_t T, int32_t H, const uint16_t* x, const uint
   if (overlap(residual_out, rb, x, rb) || overlap(norm_out, rb, x, rb))
     return fail(EP_ERR_INVALID, "an output overlaps x");
   const int V = H / 8;
-  launch_tail<1>(V, dim3((unsigned)T), (hipStream_t)stream, nullptr, nullptr, nullptr, (const ep::u32x4*)x,
-                 (const ep::u32x4*)residual, (const ep::u32x4*)gamma, eps, (ep::u32x4*)residual_out,
-                 (ep::u32x4*)norm_out, T, 1, 0);
-  return launch_status("ep_add_rmsnorm");
+  return launch_tail<1>("ep_add_rmsnorm", V, (hipStream_t)stream, nullptr, nullptr, nullptr,
+                        (const ep::u32x4*)x, (const ep::u32x4*)residual, (const ep::u32x4*)gamma, eps,
+                        (ep::u32x4*)residual_out, (ep::u32x4*)norm_out, T, 1, 0);
 }
 
 EP_EXPORT int ep_plan_splits(int32_t W, const int64_t* in_splits, int64_t* src_offsets,
