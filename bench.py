@@ -40,12 +40,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # only, comments and whitespace aside); any other build reports traffic as
 # null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "b5e1ba99e6fd415f0c441854ab45c6644d1884ac298792a827533919612cbdd9",
+    "source_sha256": "8434a109ccadf639d712af04e3d309fe87971aa5fe49251d2d15d48f74d1a0d3",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "1": {"ep_plan": 640621, "ep_dispatch": 235753173, "ep_combine": 236513952, "ep_dispatch_smooth": 144415639, "ep_combine_quant": 138726257, "ep_dispatch_int8": 135610196, "ep_combine_quant_int8": 138656945},
-        "2": {"ep_plan": 1922241, "ep_dispatch": 1059665934, "ep_combine": 1061201052, "ep_dispatch_smooth": 876050144, "ep_combine_quant": 600829029, "ep_dispatch_int8": 590488129, "ep_combine_quant_int8": 600714212, "ep_combine_add_rmsnorm": 1294119270, "ep_add_rmsnorm": 469944864},
-        "3": {"ep_all_to_all_splits": 268552624, "ep_plan_splits": 3872, "ep_dispatch_splits": 268563768},
-        "4": {"ep_plan": 3545098, "ep_dispatch": 885897025, "ep_combine": 1652699116, "ep_dispatch_smooth": 2300720158, "ep_combine_quant": 968297987, "ep_dispatch_int8": 885940828, "ep_combine_quant_int8": 968334403, "ep_combine_add_rmsnorm": 2118406075, "ep_add_rmsnorm": 939700325},
+        "1": {"ep_plan": 642741, "ep_dispatch": 235752400, "ep_combine": 236514349, "ep_dispatch_smooth": 144415991, "ep_combine_quant": 138709228, "ep_dispatch_int8": 135645207, "ep_combine_quant_int8": 138543692},
+        "2": {"ep_plan": 1920506, "ep_dispatch": 1059645698, "ep_combine": 1061201624, "ep_dispatch_smooth": 876238730, "ep_combine_quant": 600727061, "ep_dispatch_int8": 590506325, "ep_combine_quant_int8": 600737781, "ep_combine_add_rmsnorm": 1294119940, "ep_add_rmsnorm": 469944998},
+        "3": {"ep_all_to_all_splits": 268550972, "ep_plan_splits": 3872, "ep_dispatch_splits": 268568101},
+        "4": {"ep_plan": 3544492, "ep_dispatch": 885918249, "ep_combine": 1652699928, "ep_dispatch_smooth": 2301386067, "ep_combine_quant": 968867932, "ep_dispatch_int8": 886005802, "ep_combine_quant_int8": 968460284, "ep_combine_add_rmsnorm": 2118407099, "ep_add_rmsnorm": 939700562},
     },
 }
 
