@@ -114,7 +114,7 @@ def test_plan_reuse_and_determinism():
     assert_plan_equal(first, oracle.plan(ids, 60, 6, active))
 
 
-@pytest.mark.parametrize("H", [8, 128, 264, 1032, 4104, 7168])
+@pytest.mark.parametrize("H", [8, 128, 264, 1032, 4104, 7168, 65528, 65536])
 def test_dispatch_bf16_and_combine_parity(H):
     T, K, E, W = 96, 5, 20, 4
     say("dispatch/combine bf16 H", H)
