@@ -118,6 +118,17 @@ def _stream(stream=None):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+_DEVICE_COUNT = None
+
+
+def _several_devices() -> bool:
+    """More than one visible GPU (only then can a tensor be on another one)."""
+    global _DEVICE_COUNT
+    if _DEVICE_COUNT is None:
+        _DEVICE_COUNT = torch.cuda.device_count()
+    return _DEVICE_COUNT > 1
+
+
 def _ptr(t: torch.Tensor | None, dtype: torch.dtype | tuple | None = None, name: str = "tensor"):
     """Device pointer of a contiguous CUDA tensor (None -> NULL)."""
     if t is None:
@@ -130,6 +141,9 @@ def _ptr(t: torch.Tensor | None, dtype: torch.dtype | tuple | None = None, name:
             raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
     if t.numel() and not t.is_cuda:
         raise ValueError(f"{name} must live on the GPU")
+    if t.numel() and _several_devices() and t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, not on the current device "
+                         f"cuda:{torch.cuda.current_device()}")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     return ctypes.c_void_p(t.data_ptr()) if t.numel() else None
@@ -138,6 +152,13 @@ def _ptr(t: torch.Tensor | None, dtype: torch.dtype | tuple | None = None, name:
 def _check(rc: int):
     if rc != EP_OK:
         raise EPError(rc, lib.ep_last_error().decode())
+
+
+def _need_numel(t: torch.Tensor | None, n: int, name: str, shape: str):
+    """The kernels address `n` elements of `t` from its sizes alone, so a
+    smaller tensor is refused here."""
+    if t is not None and t.numel() < n:
+        raise ValueError(f"{name} must hold {shape} = {n} elements (has {t.numel()})")
 
 
 _BITS16 = (torch.bfloat16, torch.int16, torch.uint16)
@@ -169,9 +190,10 @@ def alloc_workspace(T: int, K: int, E: int, W: int, device="cuda", stream=None) 
     return ws
 
 
-@dataclass
+@dataclass(frozen=True)
 class Plan:
-    """Device outputs of ep_plan (torch tensors allocated by the caller)."""
+    """Device outputs of ep_plan (torch tensors allocated by the caller).
+    Frozen, so the checked pointer struct can be kept for later calls."""
     in_splits: torch.Tensor
     src_offsets: torch.Tensor
     out_splits: torch.Tensor
@@ -182,13 +204,33 @@ class Plan:
     pos: torch.Tensor
     occ: torch.Tensor | None
 
-    def as_struct(self) -> _PlanT:
+    def check(self, T: int, K: int, E: int, W: int) -> None:
+        """Refuses outputs smaller than ep_plan writes for these dimensions."""
+        for f, n, shape in (("in_splits", W * E, "[W][E]"), ("src_offsets", W * E, "[W][E]"),
+                            ("out_splits", W * E, "[W][E/W][W]"), ("dst_offsets", W * E, "[W][E]"),
+                            ("expert_counts", E, "[E]"), ("expert_offsets", E, "[E]"),
+                            ("rank_offsets", W + 1, "[W+1]"), ("pos", T * K, "[T][K]"),
+                            ("occ", T * K, "[T][K]")):
+            _need_numel(getattr(self, f), n, f, shape)
+
+    def as_struct(self, T: int, K: int, E: int, W: int) -> _PlanT:
+        """The C struct of device pointers, after the size check for these
+        dimensions; kept for the next call with the same dimensions and the
+        same storage (a tensor moved by an in-place resize is checked again)."""
+        key = (T, K, E, W) + tuple(None if getattr(self, f) is None else getattr(self, f).data_ptr()
+                                   for f, _ in _PlanT._fields_)
+        cached = self.__dict__.get("_struct")
+        if cached is not None and cached[0] == key:
+            return cached[1]
+        if E > 0 and W > 0:
+            self.check(T, K, E, W)
         s = _PlanT()
         for f, _ in _PlanT._fields_:
             t = getattr(self, f)
             want = torch.int32 if f in ("pos", "occ") else torch.int64
             p = _ptr(t, want, f)
             setattr(s, f, None if p is None else p.value)
+        object.__setattr__(self, "_struct", (key, s))
         return s
 
 
@@ -215,7 +257,10 @@ def ep_plan(topk_ids: torch.Tensor, E: int, W: int, plan: Plan, workspace: torch
             pad_empty_experts: bool = False, expert_token_nums: torch.Tensor | None = None,
             expert_token_nums_type: int = 1) -> Plan:
     T, K = topk_ids.shape
-    st = plan.as_struct()
+    _need_numel(active, T, "active", "[T]")
+    _need_numel(active_copies, T * K, "active_copies", "[T][K]")
+    _need_numel(expert_token_nums, E, "expert_token_nums", "[E]")
+    st = plan.as_struct(T, K, E, W)
     opts = None
     if (active_copies is not None or major_align != 1 or pad_empty_experts
             or expert_token_nums is not None):
@@ -246,6 +291,11 @@ def ep_dispatch(x: torch.Tensor, pos: torch.Tensor, expand_x: torch.Tensor,
     row_dt = _BITS16 if out_dtype == EP_BF16 else _BITS8
     if expand_x.dim() != 2 or expand_x.shape[1] != H:
         raise ValueError("expand_x must be [cap_rows][H]")
+    cap = expand_x.shape[0]
+    if out_dtype != EP_BF16:
+        _need_numel(expand_scales, cap, "expand_scales", "[cap_rows]")
+    _need_numel(weights, T * K, "weights", "[T][K]")
+    _need_numel(expand_weights, cap, "expand_weights", "[cap_rows]")
     _check(lib.ep_dispatch(T, K, H, _ptr(x, _BITS16, "x"), _ptr(pos, torch.int32, "pos"), out_dtype,
                            _ptr(expand_x, row_dt, "expand_x"),
                            _ptr(expand_scales, torch.float32, "expand_scales"),
@@ -266,6 +316,7 @@ def ep_dispatch_smooth(x: torch.Tensor, topk_ids: torch.Tensor, pos: torch.Tenso
         raise ValueError("smooth_scales must be [E][H]")
     if expand_x.dim() != 2 or expand_x.shape[1] != H:
         raise ValueError("expand_x must be [cap_rows][H]")
+    _need_numel(expand_scales, expand_x.shape[0], "expand_scales", "[cap_rows]")
     _check(lib.ep_dispatch_smooth(
         T, K, smooth_scales.shape[0], H, _ptr(x, _BITS16, "x"),
         _ptr(topk_ids, torch.int32, "topk_ids"), _ptr(pos, torch.int32, "pos"),
@@ -348,8 +399,17 @@ def alloc_splits_plan(W: int, device="cuda") -> SplitsPlan:
                       torch.empty((W, W), **i64), torch.empty(W + 1, **i64))
 
 
+def _check_splits_plan(plan: SplitsPlan, W: int):
+    for f, n, shape in (("src_offsets", W * W, "[W][W]"), ("out_splits", W * W, "[W][W]"),
+                        ("dst_offsets", W * W, "[W][W]"), ("rank_offsets", W + 1, "[W+1]")):
+        _need_numel(getattr(plan, f), n, f, shape)
+
+
 def ep_plan_splits(in_splits: torch.Tensor, plan: SplitsPlan, stream=None) -> SplitsPlan:
     W = in_splits.shape[0]
+    if tuple(in_splits.shape) != (W, W):
+        raise ValueError("in_splits must be [W][W]")
+    _check_splits_plan(plan, W)
     _check(lib.ep_plan_splits(W, _ptr(in_splits, torch.int64, "in_splits"),
                               _ptr(plan.src_offsets, torch.int64, "src_offsets"),
                               _ptr(plan.out_splits, torch.int64, "out_splits"),
@@ -364,6 +424,7 @@ def ep_dispatch_splits(inp: torch.Tensor, plan: SplitsPlan, out: torch.Tensor, s
     stride = inp[0, 0].numel() * inp.element_size() if R else 16
     if out.shape[0] != W * R or (R and out[0].numel() * out.element_size() != stride):
         raise ValueError("out must hold W*R rows of the input's row size")
+    _check_splits_plan(plan, W)
     _check(lib.ep_dispatch_splits(W, R, stride, _ptr(inp, name="in"),
                                   _ptr(plan.src_offsets, torch.int64, "src_offsets"),
                                   _ptr(plan.out_splits, torch.int64, "out_splits"),
@@ -382,6 +443,8 @@ def ep_all_to_all_splits(in_splits: torch.Tensor, inp: torch.Tensor, out: torch.
     stride = inp[0, 0].numel() * inp.element_size() if R else 16
     if out.shape[0] != W * R or (R and out[0].numel() * out.element_size() != stride):
         raise ValueError("out must hold W*R rows of the input's row size")
+    if plan is not None:
+        _check_splits_plan(plan, W)
     g = (lambda f: _ptr(getattr(plan, f), torch.int64, f)) if plan is not None else (lambda f: None)
     _check(lib.ep_all_to_all_splits(W, R, stride, _ptr(in_splits, torch.int64, "in_splits"),
                                     _ptr(inp, name="in"), _ptr(out, name="out"), g("src_offsets"),
