@@ -200,6 +200,12 @@ int id_bits_for(int E) {
   return b;
 }
 
+// Clears the given bits of the device error word, keeping any other bit a
+// kernel on another stream raised since they were read.
+__global__ void clear_error_bits_kernel(unsigned int bits) {
+  __hip_atomic_fetch_and(&ep::g_device_error, ~bits, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
 __global__ void fill_zero_kernel(uint32_t* p, size_t n) {
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
     p[i] = 0;
@@ -833,9 +839,15 @@ EP_EXPORT int ep_device_error(void* stream, int32_t* code) {
   unsigned int v = 0;
   e = hipMemcpyFromSymbol(&v, HIP_SYMBOL(ep::g_device_error), sizeof v, 0, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return fail(EP_ERR_HIP, "reading the device error word failed: %s", hipGetErrorString(e));
-  const unsigned int zero = 0;
-  e = hipMemcpyToSymbol(HIP_SYMBOL(ep::g_device_error), &zero, sizeof zero, 0, hipMemcpyHostToDevice);
-  if (e != hipSuccess) return fail(EP_ERR_HIP, "clearing the device error word failed: %s", hipGetErrorString(e));
+  if (v != 0) {
+    // Only the bits just read are cleared (an atomic AND on the device), so
+    // a bit raised meanwhile by a kernel on another stream is kept for the
+    // next call.
+    hipLaunchKernelGGL(clear_error_bits_kernel, dim3(1), dim3(1), 0, (hipStream_t)stream, v);
+    e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamSynchronize((hipStream_t)stream);
+    if (e != hipSuccess) return fail(EP_ERR_HIP, "clearing the device error word failed: %s", hipGetErrorString(e));
+  }
   *code = (int32_t)v;
   return ok();
 }

@@ -314,7 +314,9 @@ const char *ep_last_error(void);
 
 /* Synchronises `stream`, then returns in *code the device error bits
  * (EP_DEVERR_*) raised on the current device since the previous call, and
- * clears them. */
+ * clears those bits (an atomic AND enqueued on `stream`, then waited for):
+ * a bit a kernel on another stream raises meanwhile stays set for the next
+ * call. */
 int ep_device_error(void *stream, int32_t *code);
 
 #ifdef __cplusplus

@@ -97,6 +97,27 @@ def test_plan_invalid_ids_are_dropped_and_flagged():
     g.run_plan()
     assert_plan_equal(g.plan_host(), want)
     assert ep.ep_device_error() == ep.EP_DEVERR_BAD_EXPERT == want.err
+    assert ep.ep_device_error() == 0          # read once, then cleared
+
+
+def test_device_error_bits_accumulate_until_read():
+    """Two kinds of data error raised by two launches before one read: both
+    bits come back together, and the read clears exactly those."""
+    say("device error word")
+    assert ep.ep_device_error() == 0
+    ids = np.zeros((8, 2), np.int32)
+    ids[5, 1] = 99                            # expert id outside [0, 4)
+    g = GpuPath(ids, 4, 2)
+    g.run_plan()
+    send = np.array([[1, 3], [2, 2]], np.int64)
+    inp = np.arange(2 * 4 * 8, dtype=np.int32).reshape(2, 4, 8)
+    sp = ep.alloc_splits_plan(2)
+    ep.ep_plan_splits(dev(send), sp)
+    sp.src_offsets[1, 0] = 3                  # would read past rank 0's 4 rows
+    out = torch.full((8, 8), -1, dtype=torch.int32, device="cuda")
+    ep.ep_dispatch_splits(dev(inp), sp, out)
+    assert ep.ep_device_error() == ep.EP_DEVERR_BAD_EXPERT | ep.EP_DEVERR_SPLITS
+    assert ep.ep_device_error() == 0
 
 
 def test_plan_reuse_and_determinism():
