@@ -40,12 +40,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # only, comments and whitespace aside); any other build reports traffic as
 # null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "8434a109ccadf639d712af04e3d309fe87971aa5fe49251d2d15d48f74d1a0d3",
+    "source_sha256": "3f2acaae9f678f1ce2bd3238d6b4ecfb01d4cebba2989e7d59287e3f3c39448d",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "1": {"ep_plan": 642741, "ep_dispatch": 235752400, "ep_combine": 236514349, "ep_dispatch_smooth": 144415991, "ep_combine_quant": 138709228, "ep_dispatch_int8": 135645207, "ep_combine_quant_int8": 138543692},
-        "2": {"ep_plan": 1920506, "ep_dispatch": 1059645698, "ep_combine": 1061201624, "ep_dispatch_smooth": 876238730, "ep_combine_quant": 600727061, "ep_dispatch_int8": 590506325, "ep_combine_quant_int8": 600737781, "ep_combine_add_rmsnorm": 1294119940, "ep_add_rmsnorm": 469944998},
-        "3": {"ep_all_to_all_splits": 268550972, "ep_plan_splits": 3872, "ep_dispatch_splits": 268568101},
-        "4": {"ep_plan": 3544492, "ep_dispatch": 885918249, "ep_combine": 1652699928, "ep_dispatch_smooth": 2301386067, "ep_combine_quant": 968867932, "ep_dispatch_int8": 886005802, "ep_combine_quant_int8": 968460284, "ep_combine_add_rmsnorm": 2118407099, "ep_add_rmsnorm": 939700562},
+        "1": {"ep_plan": 637548, "ep_dispatch": 235744802, "ep_combine": 236513995, "ep_dispatch_smooth": 144419496, "ep_combine_quant": 138809723, "ep_dispatch_int8": 135637233, "ep_combine_quant_int8": 138469883},
+        "2": {"ep_plan": 1921824, "ep_dispatch": 1059693272, "ep_combine": 1061201370, "ep_dispatch_smooth": 875706941, "ep_combine_quant": 600931301, "ep_dispatch_int8": 590509177, "ep_combine_quant_int8": 600623109, "ep_combine_add_rmsnorm": 1294105101, "ep_add_rmsnorm": 469938815},
+        "3": {"ep_all_to_all_splits": 268542893, "ep_plan_splits": 5920, "ep_dispatch_splits": 268605454},
+        "4": {"ep_plan": 3540153, "ep_dispatch": 885924901, "ep_combine": 1652699691, "ep_dispatch_smooth": 2301358161, "ep_combine_quant": 969623077, "ep_dispatch_int8": 885975845, "ep_combine_quant_int8": 968665477, "ep_combine_add_rmsnorm": 2118406627, "ep_add_rmsnorm": 939694403},
     },
 }
 
