@@ -55,7 +55,10 @@ PLAN_CASES = [
     (8, 3, 6, 2, 0.0, 7, "dup"),            # tile smaller than a wave
     (20000, 7, 14, 2, 0.2, 8, "dup"),       # 2 ranks x 35 tiles
     (8448, 16, 1024, 2, 0.1, 9, "distinct"),  # 66 tiles x 1024 experts: look-back path
-    (131072, 8, 64, 8, 0.0, 10, "dup"),     # 512 tiles: look-back path (windowed)
+    (8192, 16, 1024, 2, 0.1, 11, "distinct"),  # 64 x 1024 = 65536 descriptors: fused, at its limit
+    (131072, 8, 64, 8, 0.0, 10, "dup"),     # 512 tiles: fused with two tiles per CU (all of MI355X)
+    (131584, 8, 64, 8, 0.0, 13, "dup"),     # 520 tiles, past what runs at once: look-back path
+    (131072, 8, 256, 8, 0.0, 12, "dup"),    # 512 tiles x 256 experts: look-back, walking windows
 ]
 
 
