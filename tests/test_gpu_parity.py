@@ -422,3 +422,69 @@ def test_fused_splits_config3_full():
     assert (host(out, np.uint16) == want_out).all()
     for f in ("src_offsets", "out_splits", "dst_offsets", "rank_offsets"):
         assert (host(getattr(sp, f)) == getattr(want, f)).all(), f
+
+
+def test_rows_past_capacity_are_dropped_and_flagged():
+    """A position at or past cap_rows (other than -1) is a caller error: every
+    row kernel drops that copy, as if its position were -1, and raises
+    EP_DEVERR_BAD_ROW; everything else is computed as usual."""
+    say("positions past capacity")
+    rng = np.random.default_rng(21)
+    T, K, H, E = 12, 3, 64, 4
+    cap = T * K
+    pos = rng.permutation(cap).astype(np.int32).reshape(T, K)
+    pos[2, 1] = cap                 # one past the end
+    pos[7, 0] = 1 << 30             # far past it
+    pos[9, 2] = -1                  # an ordinary inactive copy
+    dropped = np.where(pos >= cap, -1, pos).astype(np.int32)
+    x = workloads.bf16_bits_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    w = rng.random((T, K)).astype(np.float32)
+    ids = rng.integers(0, E, (T, K)).astype(np.int32)
+
+    def flagged():
+        return ep.ep_device_error() == ep.EP_DEVERR_BAD_ROW
+
+    ex = torch.full((cap, H), 0x5A5A, dtype=torch.int16, device="cuda")
+    ep.ep_dispatch(dev(x), dev(pos), ex)
+    assert flagged()
+    assert (host(ex, np.uint16) == oracle.dispatch_bf16(x, dropped, cap, fill=0x5A5A)).all()
+
+    q = torch.full((cap, H), 0x33, dtype=torch.uint8, device="cuda")
+    sc = torch.full((cap,), -1.0, device="cuda")
+    ep.ep_dispatch(dev(x), dev(pos), q, sc, out_dtype=ep.EP_FP8_E4M3FN)
+    assert flagged()
+    want_q, want_s = oracle.dispatch_fp8(x, dropped, cap, fill_q=0x33, fill_scale=-1.0)
+    assert (host(q) == want_q).all() and (host(sc).view(np.uint32) == want_s.view(np.uint32)).all()
+
+    smooth = workloads.smooth_scales(E, H, 3)
+    q.fill_(0x33)
+    sc.fill_(-1.0)
+    ep.ep_dispatch_smooth(dev(x), dev(ids), dev(pos), dev(smooth), q, sc, out_dtype=ep.EP_INT8)
+    assert flagged()
+    want_q, want_s = oracle.dispatch_quant(x, ids, dropped, E, oracle.Q_INT8, cap, smooth,
+                                           fill_q=0x33, fill_scale=-1.0)
+    assert (host(q) == want_q).all() and (host(sc).view(np.uint32) == want_s.view(np.uint32)).all()
+
+    y = workloads.bf16_bits_from_f32(rng.standard_normal((cap, H)).astype(np.float32))
+    out = torch.full((T, H), 0x1234, dtype=torch.int16, device="cuda")
+    ep.ep_combine(dev(y), dev(pos), dev(w), out)
+    assert flagged()
+    assert (host(out, np.uint16) == oracle.combine(y, dropped, w)).all()
+
+    ident = np.arange(cap, dtype=np.int32)[:, None]
+    codes, scales = oracle.dispatch_quant(y, np.zeros_like(ident), ident, 1, oracle.Q_FP8, cap)
+    ep.ep_combine_quant(dev(codes), dev(scales), dev(pos), dev(w), out, code_dtype=ep.EP_FP8_E4M3FN)
+    assert flagged()
+    want = oracle.combine_quant(codes, oracle.Q_FP8, scales, dropped, w)
+    assert (host(out, np.uint16) == want).all()
+
+    res = workloads.bf16_bits_from_f32(rng.standard_normal((T, H)).astype(np.float32))
+    gamma = workloads.bf16_bits_from_f32((1 + 0.1 * rng.standard_normal(H)).astype(np.float32))
+    ro = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    no = torch.empty_like(ro)
+    ep.ep_combine_add_rmsnorm(dev(y), dev(pos), dev(w), dev(res), dev(gamma), 1e-6, ro, no)
+    assert flagged()
+    want_ro, want_no = oracle.combine_add_rmsnorm(y, dropped, w, res, gamma, 1e-6)
+    assert (host(ro, np.uint16) == want_ro).all()
+    assert bf16_ulp_distance(host(no, np.uint16), want_no).max() <= 1
+    assert ep.ep_device_error() == 0
