@@ -488,3 +488,22 @@ def test_rows_past_capacity_are_dropped_and_flagged():
     assert (host(ro, np.uint16) == want_ro).all()
     assert bf16_ulp_distance(host(no, np.uint16), want_no).max() <= 1
     assert ep.ep_device_error() == 0
+
+
+def test_plan_with_a_stale_ticket_raises_stall_then_recovers():
+    """The look-back plan's tiles take tickets from the workspace header; a
+    ticket past the last tile (a workspace never initialised) makes every
+    tile raise EP_DEVERR_PLAN_STALL and return at once, without waiting.
+    The finalize kernel resets the ticket, so the next call is exact again."""
+    say("plan stall flag")
+    T, K, E, W = 8448, 16, 1024, 2          # 66 tiles x 1024 experts: the look-back path
+    ids, active = random_case(T, K, E, W, 0.0, 9, "distinct")
+    want = oracle.plan(ids, E, W, active)
+    g = GpuPath(ids, E, W, active)
+    assert ep.ep_device_error() == 0
+    g.ws.view(torch.int32)[0] = 1000        # the ticket word, far past tile 65
+    g.run_plan()
+    assert ep.ep_device_error() == ep.EP_DEVERR_PLAN_STALL
+    g.run_plan()
+    assert_plan_equal(g.plan_host(), want)
+    assert ep.ep_device_error() == 0
