@@ -18,10 +18,15 @@
  *    uint8_t codes.
  *  - `stream` is a hipStream_t (NULL = the legacy default stream).  Every
  *    call only enqueues work on it; outputs are ready when the stream
- *    reaches that point.
+ *    reaches that point.  A call may enqueue several kernels in order (the
+ *    plan's look-back path takes two; a row kernel whose grid would exceed
+ *    one launch's 2^32 - 1 work-items runs over token slices), all on
+ *    `stream`, so a captured graph holds them all.
  *  - Return value: an ep_status.  Argument checks happen on the host before
- *    anything is enqueued; on a non-OK return nothing was enqueued and
+ *    anything is enqueued; when a check fails nothing was enqueued, and
  *    ep_last_error() describes the first failed check (thread-local).
+ *    EP_ERR_HIP reports a failed launch; kernels enqueued by the same call
+ *    before it may already have run.
  *    Status classes follow the page above's return codes: null pointer,
  *    invalid value / dtype, unsupported shape.
  *  - Data errors that only the device can see (an expert id outside [0, E)
