@@ -45,7 +45,7 @@ def random_case(T, K, E, W, mask_frac, seed, routing="dup"):
 
 PLAN_CASES = [
     # T, K, E, W, mask, seed, routing       what it stresses
-    (64, 2, 8, 2, 0.0, 0, "distinct"),      # config-0 shape
+    (64, 2, 8, 2, 0.0, 0, "distinct"),      # the T=64 latency workload
     (3000, 5, 60, 6, 0.3, 1, "dup"),        # ragged tiles: Tw=500 -> 409 + 91 tokens
     (64, 16, 1024, 4, 0.0, 2, "distinct"),  # largest K and E
     (4096, 1, 1, 1, 0.5, 3, "dup"),         # E = 1, K = 1, one rank
@@ -328,9 +328,9 @@ def test_splits_bad_plan_is_flagged():
     assert (host(out) == want).all()
 
 
-def test_splits_config3_full():
+def test_splits_all_to_all_workload_full():
     cfg = workloads.WORKLOADS[3]
-    say("splits config 3 full", cfg)
+    say("splits W8 R4096 H2048 in full", cfg)
     send, inp = workloads.splits_inputs(cfg)
     sp, out = run_splits(send, inp)
     want = oracle.a2a_plan(send)
@@ -411,9 +411,9 @@ def test_fused_splits_bad_matrix_is_flagged():
     assert (host(out) == want_out).all()
 
 
-def test_fused_splits_config3_full():
+def test_fused_splits_all_to_all_workload_full():
     cfg = workloads.WORKLOADS[3]
-    say("fused splits config 3 full", cfg)
+    say("fused splits W8 R4096 H2048 in full", cfg)
     send, inp = workloads.splits_inputs(cfg)
     sp, out = run_fused_splits(send, inp)
     want = oracle.a2a_plan(send)

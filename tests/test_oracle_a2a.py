@@ -113,7 +113,7 @@ def test_random_matches_padded_even(seed):
         assert (per_rank(out, sp, r) == ref[r]).all()
 
 
-def test_config3_send_matrix():
+def test_all_to_all_workload_send_matrix():
     cfg = workloads.WORKLOADS[3]
     send = workloads.send_matrix(cfg)
     assert (send.sum(axis=1) == cfg.R).all()
