@@ -216,20 +216,28 @@ def dispatch_bf16(x_bits: np.ndarray, pos: np.ndarray, cap_rows: int,
     K = pos.shape[1]
     if out is None:
         out = np.full((cap_rows, H), 0 if fill is None else fill, dtype=np.uint16)
+    assert out.shape == (cap_rows, H) and out.dtype == np.uint16 and out.flags["C_CONTIGUOUS"]
     _check(_load().oracle_dispatch_bf16(T, K, H, _ptr(x_bits), _ptr(pos), _ptr(out), cap_rows),
            "dispatch_bf16")
     return out
 
 
 def dispatch_fp8(x_bits: np.ndarray, pos: np.ndarray, cap_rows: int,
-                 fill_q: int = 0, fill_scale: float = 0.0):
-    """Returns (q [cap_rows][H] uint8 E4M3FN codes, scales [cap_rows] float32)."""
+                 fill_q: int = 0, fill_scale: float = 0.0,
+                 q: np.ndarray | None = None, scales: np.ndarray | None = None):
+    """Returns (q [cap_rows][H] uint8 E4M3FN codes, scales [cap_rows] float32).
+    With `q` and `scales` given (C-contiguous, [cap_rows][H] uint8 and
+    [cap_rows] float32) the rows are written there and the rest is kept."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     pos = np.ascontiguousarray(pos, dtype=np.int32)
     T, H = x_bits.shape
     K = pos.shape[1]
-    q = np.full((cap_rows, H), fill_q, dtype=np.uint8)
-    scales = np.full(cap_rows, fill_scale, dtype=np.float32)
+    if q is None:
+        q = np.full((cap_rows, H), fill_q, dtype=np.uint8)
+    if scales is None:
+        scales = np.full(cap_rows, fill_scale, dtype=np.float32)
+    assert q.shape == (cap_rows, H) and q.dtype == np.uint8 and q.flags["C_CONTIGUOUS"]
+    assert scales.shape == (cap_rows,) and scales.dtype == np.float32 and scales.flags["C_CONTIGUOUS"]
     scratch = np.zeros(H, np.uint8)
     _check(_load().oracle_dispatch_fp8(T, K, H, _ptr(x_bits), _ptr(pos), _ptr(q),
                                        _ptr(scales), cap_rows, _ptr(scratch)), "dispatch_fp8")

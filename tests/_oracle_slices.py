@@ -1,0 +1,66 @@
+"""The oracle over token slices on host threads, for full-size parity.
+
+Each call below runs the serial C oracle on contiguous slices of tokens in
+parallel (ctypes releases the interpreter lock during the call).  Slices
+write disjoint rows: a live copy's position is unique, and the combine's
+output rows are the slice's own tokens.  The arithmetic is the oracle's,
+unchanged; only the work is split.
+"""
+from __future__ import annotations
+
+import os
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+
+import oracle
+
+
+def host_threads() -> int:
+    """Host threads for the oracle (at most 16, the CPU share of a one-GPU machine)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _slices(T: int, n: int):
+    b = np.linspace(0, T, n + 1).astype(int)
+    return [(int(lo), int(hi)) for lo, hi in zip(b[:-1], b[1:]) if hi > lo]
+
+
+def _run(fn, T: int):
+    n = host_threads()
+    with ThreadPoolExecutor(n) as pool:
+        list(pool.map(lambda s: fn(*s), _slices(T, 4 * n)))
+
+
+def dispatch_bf16(x: np.ndarray, pos: np.ndarray, cap_rows: int, fill: int) -> np.ndarray:
+    """expandX [cap_rows][H] uint16; rows no copy names hold `fill`."""
+    T, H = x.shape
+    out = np.full((cap_rows, H), fill, np.uint16)
+    _run(lambda lo, hi: oracle.dispatch_bf16(x[lo:hi], pos[lo:hi], cap_rows, out=out), T)
+    return out
+
+
+def dispatch_fp8(x: np.ndarray, pos: np.ndarray, cap_rows: int, fill_q: int, fill_scale: float):
+    """(codes [cap_rows][H] uint8, scales [cap_rows] float32); rows no copy
+    names hold the fills."""
+    T, H = x.shape
+    q = np.full((cap_rows, H), fill_q, np.uint8)
+    sc = np.full(cap_rows, fill_scale, np.float32)
+    _run(lambda lo, hi: oracle.dispatch_fp8(x[lo:hi], pos[lo:hi], cap_rows, q=q, scales=sc), T)
+    return q, sc
+
+
+def combine(y: np.ndarray, pos: np.ndarray, weights: np.ndarray) -> np.ndarray:
+    """out [T][H] uint16 for every token."""
+    T = pos.shape[0]
+    out = np.empty((T, y.shape[1]), np.uint16)
+
+    def run(lo, hi):
+        out[lo:hi] = oracle.combine(y, pos[lo:hi], weights[lo:hi])
+
+    _run(run, T)
+    return out

@@ -1,12 +1,20 @@
-"""Full-size parity in the benchmark's launch configuration.
+"""Full-size parity in the benchmark's launch configuration, element by element.
 
 For the three MoE workloads (T=4096/H=4096/E=64/K=6/W=8 uniform;
 T=8192/H=7168/E=256/K=8/W=16 Zipf(1.2) with empty experts;
-T=16384/H=7168/E=256/K=8/W=32, 25% of tokens masked, fp8 dispatch) the whole
-plan is compared with the oracle bit for bit; dispatch and combine are
-checked on a seeded sample of tokens, the oracle evaluating exactly those
-tokens (a sub-problem holding their rows), plus the properties that hold at
-any size: rows past N keep their sentinel, every live row is written.
+T=16384/H=7168/E=256/K=8/W=32, 25% of tokens masked, fp8 dispatch) every
+output is compared with the oracle over the whole workload:
+
+- the whole plan, bit for bit;
+- every row of the expandX buffer, the rows past N included (they must keep
+  their sentinel): bf16 rows bit for bit, or every fp8 code and every fp32
+  scale bit for bit;
+- every output row of the combine, at 0 bf16 ulp.
+
+The oracle runs over token slices on host threads (tests/_oracle_slices.py).
+The T=8192 workload is also combined over independent random expert rows,
+so that the K inputs of a token differ (the dispatched rows are K copies of
+the token's own row).
 """
 import numpy as np
 import pytest
@@ -15,30 +23,45 @@ import torch
 import combine_ep_plan_02_amd as ep
 import oracle
 import workloads
+import _oracle_slices as par
 from _gpu_util import GpuPath, assert_plan_equal, bf16_ulp_distance, dev, host
 
 pytestmark = pytest.mark.gpu
 
-N_SAMPLE = 384
+SENTINEL_BF16 = 0x7777
+SENTINEL_Q = 0x33
+SENTINEL_SCALE = -1.0
 
 
 def say(*a):
     print(*a, flush=True)
 
 
-def sample_tokens(T, seed):
-    rng = np.random.default_rng(seed + 777)
-    s = rng.choice(T, size=min(N_SAMPLE, T), replace=False)
-    return np.sort(np.concatenate([s, [0, T - 1]]))
+def assert_rows_equal(got: np.ndarray, want: np.ndarray, what: str):
+    assert got.shape == want.shape, (what, got.shape, want.shape)
+    if np.array_equal(got, want):
+        return
+    bad = np.argwhere(got != want)
+    r = bad[0][0]
+    raise AssertionError(f"{what}: {len(bad)} elements differ in {len(np.unique(bad[:, 0]))} rows; "
+                         f"first at {bad[0].tolist()}: got {got[tuple(bad[0])]}, "
+                         f"want {want[tuple(bad[0])]} (row {r})")
 
 
-def sub_problem(pos, tokens):
-    """Remaps the sampled tokens' live positions to rows 0..m-1."""
-    sub = pos[tokens].copy()
-    live = sub >= 0
-    rows = sub[live]
-    sub[live] = np.arange(rows.size, dtype=np.int32)
-    return sub, rows
+def assert_combine_exact(got: np.ndarray, want: np.ndarray, what: str):
+    d = bf16_ulp_distance(got, want)
+    n = int((d > 0).sum())
+    assert n == 0, f"{what}: {n} of {d.size} elements differ (max {int(d.max())} ulp), " \
+                   f"first at {np.argwhere(d > 0)[0].tolist()}"
+
+
+def run_combine(y_dev, pos_dev, w_np):
+    T = pos_dev.shape[0]
+    H = y_dev.shape[1]
+    out = torch.empty((T, H), dtype=torch.int16, device="cuda")
+    ep.ep_combine(y_dev, pos_dev, dev(w_np), out)
+    torch.cuda.synchronize()
+    return host(out, np.uint16)
 
 
 @pytest.mark.parametrize("idx", [1, 2, 4])
@@ -56,54 +79,57 @@ def test_fullsize_workload(idx):
     say("  plan ok, N =", N)
 
     x = dev(inp.x)
-    toks = sample_tokens(cfg.T, idx)
-    sub_pos, rows = sub_problem(want.pos, toks)
     if not cfg.fp8:
-        ex = torch.empty((cap, cfg.H), dtype=torch.int16, device="cuda")
-        if N < cap:
-            ex[N:].fill_(0x7777)
+        ex = torch.full((cap, cfg.H), SENTINEL_BF16, dtype=torch.int16, device="cuda")
         ep.ep_dispatch(x, g.plan.pos, ex)
         torch.cuda.synchronize()
-        # sampled tokens: every live copy's row equals the oracle's dispatch of it
-        want_sub = oracle.dispatch_bf16(inp.x[toks], sub_pos, rows.size)
-        got_rows = host(ex[dev(rows.astype(np.int64))], np.uint16)
-        assert (got_rows == want_sub).all()
-        if N < cap:
-            assert bool((ex[N:] == 0x7777).all())
-        say("  dispatch ok")
-        y_dev, y_sub = ex, want_sub          # the combine reads the dispatched rows back
+        want_ex = par.dispatch_bf16(inp.x, want.pos, cap, SENTINEL_BF16)
+        assert_rows_equal(host(ex, np.uint16), want_ex, "expandX (bf16)")
+        say(f"  dispatch ok: all {cap} rows ({N} written, {cap - N} sentinels)")
+        y_dev, y_host = ex, want_ex      # the combine reads the dispatched rows back
     else:
-        q = torch.empty((cap, cfg.H), dtype=torch.uint8, device="cuda")
-        sc = torch.full((cap,), -1.0, dtype=torch.float32, device="cuda")
-        if N < cap:
-            q[N:].fill_(0x33)
+        q = torch.full((cap, cfg.H), SENTINEL_Q, dtype=torch.uint8, device="cuda")
+        sc = torch.full((cap,), SENTINEL_SCALE, dtype=torch.float32, device="cuda")
         ep.ep_dispatch(x, g.plan.pos, q, sc, out_dtype=ep.EP_FP8_E4M3FN)
         torch.cuda.synchronize()
-        want_q, want_s = oracle.dispatch_fp8(inp.x[toks], sub_pos, rows.size)
-        ridx = dev(rows.astype(np.int64))
-        assert (host(q[ridx]) == want_q).all()
-        assert (host(sc[ridx]).view(np.uint32) == want_s.view(np.uint32)).all()
-        if N < cap:
-            assert bool((q[N:] == 0x33).all()) and bool((sc[N:] == -1.0).all())
-        # every live row got a scale (no row was skipped)
-        assert bool((sc[:N] >= 0).all())
-        say("  fp8 dispatch ok")
+        want_q, want_s = par.dispatch_fp8(inp.x, want.pos, cap, SENTINEL_Q, SENTINEL_SCALE)
+        assert_rows_equal(host(sc).view(np.uint32), want_s.view(np.uint32), "fp8 scales")
+        assert_rows_equal(host(q), want_q, "fp8 codes")
+        say(f"  fp8 dispatch ok: all {cap} rows of codes and scales ({N} written)")
+        del q, sc, want_q, want_s
         # the bf16 combine reads synthetic expert outputs in expandX layout
         y_host = np.zeros((cap, cfg.H), np.uint16)
         y_host[:N] = workloads.expert_outputs(N, cfg.H, cfg.seed)
         y_dev = dev(y_host)
-        y_sub = y_host[rows]
-        del y_host
+    del x
 
-    out = torch.empty((cfg.T, cfg.H), dtype=torch.int16, device="cuda")
-    ep.ep_combine(y_dev, g.plan.pos, dev(inp.weights), out)
-    torch.cuda.synchronize()
-    want_out = oracle.combine(y_sub, sub_pos, inp.weights[toks])
-    d = bf16_ulp_distance(host(out[dev(toks.astype(np.int64))], np.uint16), want_out)
-    assert d.max() <= 1
-    assert (d == 0).all(), f"{int((d > 0).sum())} elements 1 ulp apart"
+    got = run_combine(y_dev, g.plan.pos, inp.weights)
+    want_out = par.combine(y_host, want.pos, inp.weights)
+    assert_combine_exact(got, want_out, "combine")
     if inp.active is not None:
-        dead = np.nonzero(inp.active == 0)[0][:64]
-        assert (host(out[dev(dead.astype(np.int64))]) == 0).all()
+        dead = inp.active == 0
+        assert (got[dead] == 0).all(), "an inactive token's row is not +0"
+    say(f"  combine ok: all {cfg.T} rows at 0 ulp")
     assert ep.ep_device_error() == 0
-    say("  combine ok")
+
+
+def test_fullsize_zipf_combine_of_distinct_rows():
+    """T=8192, H=7168, E=256, K=8, W=16 (Zipf): the combine over independent
+    N(0,1) expert rows, so each token sums K different rows; every output
+    row against the oracle at 0 ulp."""
+    cfg = workloads.WORKLOADS[2]
+    say("full-size combine over distinct rows:", cfg.name)
+    ep.ep_device_error()
+    inp = workloads.moe_inputs(cfg, with_x=False)
+    want = oracle.plan(inp.ids, cfg.E, cfg.W, inp.active)
+    N = want.n_rows
+    g = GpuPath(inp.ids, cfg.E, cfg.W, inp.active)
+    g.run_plan()
+    assert_plan_equal(g.plan_host(), want)
+    y_host = np.zeros((cfg.cap_rows, cfg.H), np.uint16)
+    y_host[:N] = workloads.expert_outputs(N, cfg.H, cfg.seed + 50)
+    got = run_combine(dev(y_host), g.plan.pos, inp.weights)
+    want_out = par.combine(y_host, want.pos, inp.weights)
+    assert_combine_exact(got, want_out, "combine of distinct rows")
+    say(f"  combine ok: all {cfg.T} rows at 0 ulp")
+    assert ep.ep_device_error() == 0
