@@ -37,6 +37,9 @@ EP_DEVERR_SPLITS = 2
 EP_DEVERR_PLAN_STALL = 4
 EP_DEVERR_BAD_ROW = 8
 
+EP_PLAN_LOOKBACK = 1
+EP_PLAN_TEST_STALL = 0x40000000
+
 _STATUS_NAMES = {1: "EP_ERR_NULLPTR", 2: "EP_ERR_INVALID", 3: "EP_ERR_UNSUPPORTED",
                  4: "EP_ERR_WORKSPACE", 5: "EP_ERR_HIP"}
 
@@ -56,7 +59,7 @@ class EPError(RuntimeError):
 class _PlanOpts(ctypes.Structure):
     _fields_ = [("active_copies", ctypes.c_void_p), ("major_align", ctypes.c_int32),
                 ("pad_empty_experts", ctypes.c_int32), ("expert_token_nums_type", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("expert_token_nums", ctypes.c_void_p)]
+                ("flags", ctypes.c_int32), ("expert_token_nums", ctypes.c_void_p)]
 
 
 class _PlanT(ctypes.Structure):
@@ -251,30 +254,40 @@ def ep_expand_rows_bound(T: int, K: int, E: int, major_align: int = 1,
     return int(lib.ep_expand_rows_bound(T, K, E, major_align, int(bool(pad_empty_experts))))
 
 
+def _plan_opts(T, K, E, active, active_copies, major_align, pad_empty_experts, expert_token_nums,
+               expert_token_nums_type, flags):
+    """Checks the per-token inputs' sizes and builds ep_plan_opts_t (None
+    when every option has its default)."""
+    _need_numel(active, T, "active", "[T]")
+    _need_numel(active_copies, T * K, "active_copies", "[T][K]")
+    _need_numel(expert_token_nums, E, "expert_token_nums", "[E]")
+    if (active_copies is None and major_align == 1 and not pad_empty_experts
+            and expert_token_nums is None and flags == 0):
+        return None
+    o = _PlanOpts()
+    p = _ptr(active_copies, (torch.uint8, torch.bool), "active_copies")
+    o.active_copies = None if p is None else p.value
+    o.major_align = int(major_align)
+    o.pad_empty_experts = int(bool(pad_empty_experts))
+    o.expert_token_nums_type = int(expert_token_nums_type)
+    o.flags = int(flags)
+    p = _ptr(expert_token_nums, torch.int64, "expert_token_nums")
+    o.expert_token_nums = None if p is None else p.value
+    return o
+
+
 def ep_plan(topk_ids: torch.Tensor, E: int, W: int, plan: Plan, workspace: torch.Tensor,
             active: torch.Tensor | None = None, stream=None, *,
             active_copies: torch.Tensor | None = None, major_align: int = 1,
             pad_empty_experts: bool = False, expert_token_nums: torch.Tensor | None = None,
-            expert_token_nums_type: int = 1) -> Plan:
+            expert_token_nums_type: int = 1, flags: int = 0) -> Plan:
     T, K = topk_ids.shape
-    _need_numel(active, T, "active", "[T]")
-    _need_numel(active_copies, T * K, "active_copies", "[T][K]")
-    _need_numel(expert_token_nums, E, "expert_token_nums", "[E]")
+    o = _plan_opts(T, K, E, active, active_copies, major_align, pad_empty_experts,
+                   expert_token_nums, expert_token_nums_type, flags)
     st = plan.as_struct(T, K, E, W)
-    opts = None
-    if (active_copies is not None or major_align != 1 or pad_empty_experts
-            or expert_token_nums is not None):
-        o = _PlanOpts()
-        p = _ptr(active_copies, (torch.uint8, torch.bool), "active_copies")
-        o.active_copies = None if p is None else p.value
-        o.major_align = int(major_align)
-        o.pad_empty_experts = int(bool(pad_empty_experts))
-        o.expert_token_nums_type = int(expert_token_nums_type)
-        p = _ptr(expert_token_nums, torch.int64, "expert_token_nums")
-        o.expert_token_nums = None if p is None else p.value
-        opts = ctypes.byref(o)
     _check(lib.ep_plan(T, K, E, W, _ptr(topk_ids, torch.int32, "topk_ids"),
-                       _ptr(active, (torch.uint8, torch.bool), "active"), opts, ctypes.byref(st),
+                       _ptr(active, (torch.uint8, torch.bool), "active"),
+                       None if o is None else ctypes.byref(o), ctypes.byref(st),
                        _ptr(workspace, name="workspace"),
                        workspace.numel() * workspace.element_size(), _stream(stream)))
     return plan

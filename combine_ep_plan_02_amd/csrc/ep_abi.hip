@@ -248,18 +248,45 @@ EP_EXPORT int64_t ep_expand_rows_bound(int32_t T, int32_t K, int32_t E, int32_t 
   return (int64_t)T * K + (int64_t)E * (pad_empty_experts ? a : a - 1);
 }
 
-EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t* topk_ids,
-                      const uint8_t* active, const ep_plan_opts_t* opts, const ep_plan_t* plan,
-                      void* workspace, size_t ws_bytes, void* stream) {
+namespace {
+
+// Where the plan kernels keep their state: the ticket, epoch and done
+// counter (header), the look-back flags, aggregates and inclusive prefixes,
+// and the one-launch path's count descriptors.
+struct PlanState {
+  uint32_t* header;
+  uint32_t* flags;
+  int32_t* aggregates;
+  int32_t* inclusive;
+  uint64_t* desc;
+};
+
+// Tiles and descriptors the one-launch plan may use.  The kernel is taken
+// only when its whole grid fits on the device at once with room to spare:
+// half of what fits (workgroups per CU by occupancy times the CU count), so
+// that a second plan, or another kernel, on another stream still leaves it
+// resident.  Its waits are bounded (a tile gives up after one spin budget),
+// so a grid kept from becoming resident ends with EP_DEVERR_PLAN_STALL
+// instead of hanging.
+bool fused_fits(int ntiles, int E) {
+  return ntiles > 0 && (int64_t)ntiles * E <= ep::kFusedMaxDescriptorsPerTile &&
+         2 * ntiles <= fused_capacity(E);
+}
+
+int check_plan_args(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t* topk_ids,
+                    const uint8_t* active, const ep_plan_opts_t* opts, const ep_plan_t* plan,
+                    ep_plan_opts_t& o) {
   int rc = check_dims(T, K, E, W);
   if (rc) return rc;
-  ep_plan_opts_t o{};
+  o = ep_plan_opts_t{};
   if (opts) o = *opts;
   if (o.major_align < 1) o.major_align = 1;
   if (o.major_align > EP_MAX_ALIGN)
     return fail(EP_ERR_UNSUPPORTED, "major_align must be <= %d (got %d)", EP_MAX_ALIGN, o.major_align);
   if (o.expert_token_nums_type != 0 && o.expert_token_nums_type != 1)
     return fail(EP_ERR_INVALID, "expert_token_nums_type must be 0 or 1 (got %d)", o.expert_token_nums_type);
+  if ((uint32_t)o.flags & ~(uint32_t)(EP_PLAN_LOOKBACK | EP_PLAN_TEST_STALL))
+    return fail(EP_ERR_INVALID, "unknown plan flags 0x%x", (unsigned)o.flags);
   if (ep_expand_rows_bound(T, K, E, o.major_align, o.pad_empty_experts) >= (int64_t)1 << 31)
     return fail(EP_ERR_UNSUPPORTED, "T*K plus the expert padding must be < 2^31");
   if (!plan) return fail(EP_ERR_NULLPTR, "plan is NULL");
@@ -268,68 +295,71 @@ EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t*
     return fail(EP_ERR_NULLPTR, "a required plan output is NULL");
   const int64_t ncopies = (int64_t)T * K;
   if (ncopies > 0 && (!topk_ids || !plan->pos)) return fail(EP_ERR_NULLPTR, "topk_ids or pos is NULL");
-  if (!workspace) return fail(EP_ERR_NULLPTR, "workspace is NULL");
-  if (!aligned(workspace, 256)) return fail(EP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
-  const PlanGeometry g = plan_geometry(T, K, W);
-  const WorkspaceLayout l = workspace_layout(g.ntiles, E);
-  if (ws_bytes < l.total)
-    return fail(EP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, l.total);
-
   const int64_t* outs64[] = {plan->in_splits, plan->src_offsets, plan->out_splits, plan->dst_offsets,
                              plan->expert_counts, plan->expert_offsets, plan->rank_offsets};
-  const size_t n64[] = {(size_t)W * E, (size_t)W * E, (size_t)W * E, (size_t)W * E, (size_t)E,
-                        (size_t)E, (size_t)W + 1};
   for (int i = 0; i < 7; ++i)
     if (!aligned(outs64[i], 8)) return fail(EP_ERR_INVALID, "plan int64 outputs must be 8-byte aligned");
   if (!aligned(topk_ids, 4) || !aligned(plan->pos, 4) || !aligned(plan->occ, 4))
     return fail(EP_ERR_INVALID, "topk_ids, pos and occ must be 4-byte aligned");
   if (!aligned(o.expert_token_nums, 8))
     return fail(EP_ERR_INVALID, "expert_token_nums must be 8-byte aligned");
-  // No output may overlap an input or another output.
+  return EP_OK;
+}
+
+// No output may overlap an input or another output (the workspace, when the
+// caller brings one, counts as both).
+int check_plan_overlaps(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t* topk_ids,
+                        const uint8_t* active, const ep_plan_opts_t& o, const ep_plan_t* plan,
+                        const void* workspace, size_t ws_bytes) {
+  const int64_t ncopies = (int64_t)T * K;
+  const size_t we = (size_t)W * E * 8;
   struct Range { const void* p; size_t n; const char* name; };
   const Range ranges[] = {
       {topk_ids, (size_t)ncopies * 4, "topk_ids"}, {active, active ? (size_t)T : 0, "active"},
       {o.active_copies, o.active_copies ? (size_t)ncopies : 0, "active_copies"},
-      {workspace, l.total, "workspace"}, {plan->pos, (size_t)ncopies * 4, "pos"},
+      {workspace, workspace ? ws_bytes : 0, "workspace"}, {plan->pos, (size_t)ncopies * 4, "pos"},
       {o.expert_token_nums, o.expert_token_nums ? (size_t)E * 8 : 0, "expert_token_nums"},
       {plan->occ, plan->occ ? (size_t)ncopies * 4 : 0, "occ"},
-      {outs64[0], n64[0] * 8, "in_splits"}, {outs64[1], n64[1] * 8, "src_offsets"},
-      {outs64[2], n64[2] * 8, "out_splits"}, {outs64[3], n64[3] * 8, "dst_offsets"},
-      {outs64[4], n64[4] * 8, "expert_counts"}, {outs64[5], n64[5] * 8, "expert_offsets"},
-      {outs64[6], n64[6] * 8, "rank_offsets"}};
+      {plan->in_splits, we, "in_splits"}, {plan->src_offsets, we, "src_offsets"},
+      {plan->out_splits, we, "out_splits"}, {plan->dst_offsets, we, "dst_offsets"},
+      {plan->expert_counts, (size_t)E * 8, "expert_counts"},
+      {plan->expert_offsets, (size_t)E * 8, "expert_offsets"},
+      {plan->rank_offsets, (size_t)(W + 1) * 8, "rank_offsets"}};
   const int nr = sizeof ranges / sizeof ranges[0];
   for (int i = 0; i < nr; ++i)
     for (int j = (i < 3 ? 3 : i + 1); j < nr; ++j)
       if (overlap(ranges[i].p, ranges[i].n, ranges[j].p, ranges[j].n))
         return fail(EP_ERR_INVALID, "%s overlaps %s", ranges[i].name, ranges[j].name);
+  return EP_OK;
+}
 
-  hipStream_t s = (hipStream_t)stream;
-  uint8_t* ws = (uint8_t*)workspace;
-  uint32_t* header = (uint32_t*)ws;
-  uint32_t* ticket = header + ep::kHeaderTicket;
-  uint32_t* flags = (uint32_t*)(ws + l.flags);
-  int32_t* aggregates = (int32_t*)(ws + l.aggregates);
-  int32_t* inclusive = (int32_t*)(ws + l.inclusive);
-
-  if (g.ntiles > 0 && (int64_t)g.ntiles * E <= ep::kFusedMaxDescriptorsPerTile &&
-      g.ntiles <= fused_capacity(E)) {
+int launch_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t* topk_ids, const uint8_t* active,
+                const ep_plan_opts_t& o, const ep_plan_t* plan, const PlanState& st, bool fused,
+                hipStream_t s) {
+  const PlanGeometry g = plan_geometry(T, K, W);
+  const int64_t ncopies = (int64_t)T * K;
+  if (fused) {
     // Single pass: every tile resident at once, counts exchanged through
-    // self-validating descriptors.
+    // self-validating descriptors.  The test hook withholds the last tile's
+    // counts and shortens the spin budget, so every tile gives up quickly.
+    const bool test_stall = (o.flags & EP_PLAN_TEST_STALL) != 0;
     const size_t lds = fused_lds_bytes(E);
-    uint64_t* desc = (uint64_t*)(ws + l.descriptors);
     hipLaunchKernelGGL(ep::plan_fused_kernel, dim3(g.ntiles), dim3(ep::kPlanThreads), lds, s, topk_ids, active,
                        o.active_copies, K, E, W, g.Tw, g.tile_tokens, g.tiles_per_rank, g.ntiles, id_bits_for(E),
                        o.major_align, o.pad_empty_experts ? 1 : 0, o.expert_token_nums_type,
-                       o.expert_token_nums, header, desc, plan->pos, plan->occ, plan->in_splits, plan->src_offsets, plan->out_splits,
-                       plan->dst_offsets, plan->expert_counts, plan->expert_offsets, plan->rank_offsets);
+                       o.expert_token_nums, st.header, st.desc, plan->pos, plan->occ, plan->in_splits,
+                       plan->src_offsets, plan->out_splits, plan->dst_offsets, plan->expert_counts,
+                       plan->expert_offsets, plan->rank_offsets, test_stall ? ep::kTestSpinLimit : ep::kSpinLimit,
+                       test_stall ? g.ntiles - 1 : -1);
     return launch_status("ep_plan (fused kernel)");
   }
+  uint32_t* ticket = st.header + ep::kHeaderTicket;
   if (g.ntiles > 0) {
     const size_t lds = (size_t)(ep::kPlanWaves + 2) * E * sizeof(int32_t);
     hipLaunchKernelGGL(ep::plan_tile_kernel, dim3(g.ntiles), dim3(ep::kPlanThreads), lds, s, topk_ids,
                        active, o.active_copies, K, E, g.Tw, g.tile_tokens, g.tiles_per_rank, g.ntiles, id_bits_for(E),
-                       plan->pos, ticket, flags, aggregates, inclusive);
-    rc = launch_status("ep_plan (tile kernel)");
+                       plan->pos, ticket, st.flags, st.aggregates, st.inclusive);
+    const int rc = launch_status("ep_plan (tile kernel)");
     if (rc) return rc;
   }
   const int64_t per_block = (int64_t)ep::kFinalizeThreads * ep::kFinalizeCopiesPerThread;
@@ -338,10 +368,33 @@ EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t*
   hipLaunchKernelGGL(ep::plan_finalize_kernel, dim3((unsigned)blocks), dim3(ep::kFinalizeThreads), 0, s,
                      topk_ids, ncopies, K, E, W, g.Tw > 0 ? g.Tw : 1, g.tiles_per_rank, g.ntiles,
                      o.major_align, o.pad_empty_experts ? 1 : 0, o.expert_token_nums_type,
-                     o.expert_token_nums, aggregates, inclusive, flags, ticket, plan->pos, plan->occ, plan->in_splits,
-                     plan->src_offsets, plan->out_splits, plan->dst_offsets, plan->expert_counts,
-                     plan->expert_offsets, plan->rank_offsets);
+                     o.expert_token_nums, st.aggregates, st.inclusive, st.flags, ticket, plan->pos, plan->occ,
+                     plan->in_splits, plan->src_offsets, plan->out_splits, plan->dst_offsets,
+                     plan->expert_counts, plan->expert_offsets, plan->rank_offsets);
   return launch_status("ep_plan (finalize kernel)");
+}
+
+}  // namespace
+
+EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t* topk_ids,
+                      const uint8_t* active, const ep_plan_opts_t* opts, const ep_plan_t* plan,
+                      void* workspace, size_t ws_bytes, void* stream) {
+  ep_plan_opts_t o;
+  int rc = check_plan_args(T, K, E, W, topk_ids, active, opts, plan, o);
+  if (rc) return rc;
+  if (!workspace) return fail(EP_ERR_NULLPTR, "workspace is NULL");
+  if (!aligned(workspace, 256)) return fail(EP_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  const PlanGeometry g = plan_geometry(T, K, W);
+  const WorkspaceLayout l = workspace_layout(g.ntiles, E);
+  if (ws_bytes < l.total)
+    return fail(EP_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", ws_bytes, l.total);
+  rc = check_plan_overlaps(T, K, E, W, topk_ids, active, o, plan, workspace, l.total);
+  if (rc) return rc;
+  uint8_t* ws = (uint8_t*)workspace;
+  const PlanState st{(uint32_t*)ws, (uint32_t*)(ws + l.flags), (int32_t*)(ws + l.aggregates),
+                     (int32_t*)(ws + l.inclusive), (uint64_t*)(ws + l.descriptors)};
+  const bool fused = !(o.flags & EP_PLAN_LOOKBACK) && fused_fits(g.ntiles, E);
+  return launch_plan(T, K, E, W, topk_ids, active, o, plan, st, fused, (hipStream_t)stream);
 }
 
 EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, const int32_t* pos,
@@ -808,20 +861,26 @@ EP_EXPORT int ep_all_to_all_splits(int32_t W, int64_t R, int64_t stride_bytes, c
           overlap(arrays[i], sizes[i], arrays[j], sizes[j]))
         return fail(EP_ERR_INVALID, "an output of the all-to-all overlaps another buffer");
     }
+  // Work split by output rows (at most W*R of them): a wave copies a run of
+  // rows of about kA2ARowsPerWaveBytes, a workgroup four runs; the grid
+  // loops over the runs when there are more than one launch holds.
   const int64_t Vr = stride_bytes / 16;
-  const int chunks = W * W;
-  int bpc = (2048 + chunks - 1) / chunks;
-  const int64_t need = (R + ep::kTokensPerBlock - 1) / ep::kTokensPerBlock;
-  if (bpc > need) bpc = (int)need;
-  if (bpc < 1) bpc = 1;
-  const dim3 grid(chunks, bpc);
+  int64_t rows_per_wave = ep::kA2ARowsPerWaveBytes / stride_bytes;
+  if (rows_per_wave < 1) rows_per_wave = 1;
+  const int64_t rows = (int64_t)W * R;
+  const int64_t per_block = rows_per_wave * ep::kTokensPerBlock;
+  const int64_t n_ranges = (rows + per_block - 1) / per_block;
+  int64_t blocks = n_ranges < ((int64_t)1 << 20) ? n_ranges : ((int64_t)1 << 20);
+  if (blocks < 1) blocks = 1;
+  const size_t lds = ((size_t)W * W + W + 1) * sizeof(int64_t);
   hipStream_t s = (hipStream_t)stream;
   const ep::u32x4* iv = (const ep::u32x4*)in;
   ep::u32x4* ov = (ep::u32x4*)out;
   const int64_t per_lane = (Vr + ep::kWave - 1) / ep::kWave;
-#define EP_A2A(U)                                                                                          \
-  hipLaunchKernelGGL((ep::all_to_all_splits_kernel<U, kCopyNtLoad, kCopyNtStore>), grid, dim3(ep::kRowThreads), \
-                     0, s, iv, ov, in_splits, src_offsets, out_splits, dst_offsets, rank_offsets, W, R, Vr)
+#define EP_A2A(U)                                                                                               \
+  hipLaunchKernelGGL((ep::all_to_all_splits_kernel<U, kCopyNtLoad, kCopyNtStore>), dim3((unsigned)blocks),        \
+                     dim3(ep::kRowThreads), lds, s, iv, ov, in_splits, src_offsets, out_splits, dst_offsets,     \
+                     rank_offsets, W, R, Vr, rows_per_wave, n_ranges)
   if (per_lane <= 1) EP_A2A(1);
   else if (per_lane <= 2) EP_A2A(2);
   else if (per_lane <= 4) EP_A2A(4);

@@ -40,6 +40,7 @@ constexpr int kPlanTileCopies = kPlanWaves * kWave * kPlanChunks;  // 2048
 constexpr uint32_t kFlagAggregate = 1u;
 constexpr uint32_t kFlagInclusive = 2u;
 constexpr int kSpinLimit = 1 << 20;  // bounded polling: the kernel always exits
+constexpr int kTestSpinLimit = 256;  // the stall test's budget (EP_PLAN_TEST_STALL)
 
 constexpr int kFinalizeThreads = 256;
 constexpr int kFinalizeCopiesPerThread = 4;
@@ -417,15 +418,24 @@ constexpr int kHeaderTicket = 0;
 constexpr int kHeaderEpoch = 1;
 constexpr int kHeaderDone = 2;
 
-__device__ __forceinline__ uint64_t wait_descriptor(const uint64_t* d, uint32_t epoch) {
+// Polls a descriptor until it carries `epoch`.  The wait is bounded per
+// thread, over all of its waits together (`budget` polls), and per tile: the
+// first thread that runs out of polls raises EP_DEVERR_PLAN_STALL and sets the
+// tile's LDS flag `stalled`, after which every wait of the tile returns at
+// once.  A tile therefore gives up within one budget in all, however many
+// descriptors are missing; its counts then read as 0 and the plan is invalid.
+__device__ __forceinline__ uint64_t wait_descriptor(const uint64_t* d, uint32_t epoch, int& budget,
+                                                    int* stalled) {
   uint64_t v = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  for (int spin = 0; (uint32_t)(v >> 32) != epoch && spin < kSpinLimit; ++spin) {
+  while ((uint32_t)(v >> 32) != epoch) {
+    if (budget <= 0 || __hip_atomic_load(stalled, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) {
+      if (__hip_atomic_exchange(stalled, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP) == 0)
+        raise_device_error(kErrPlanStall);
+      return 0;
+    }
+    --budget;
     __builtin_amdgcn_s_sleep(1);
     v = __hip_atomic_load(d, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  if ((uint32_t)(v >> 32) != epoch) {
-    raise_device_error(kErrPlanStall);
-    return 0;
   }
   return v & 0xffffffffull;
 }
@@ -471,7 +481,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
     int64_t* __restrict__ in_splits, int64_t* __restrict__ src_offsets,
     int64_t* __restrict__ out_splits, int64_t* __restrict__ dst_offsets,
     int64_t* __restrict__ expert_counts, int64_t* __restrict__ expert_offsets,
-    int64_t* __restrict__ rank_offsets) {
+    int64_t* __restrict__ rank_offsets, int spin_limit, int withhold_tile) {
   extern __shared__ int32_t lds[];
   int32_t* hist = lds;                       // [kPlanWaves][E]
   int32_t* tot = hist + kPlanWaves * E;      // [E] all tiles -> expert offsets
@@ -481,11 +491,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
   int32_t* rbg = rin + E;                    // [E] tiles before rank blockIdx.x
   int32_t* cnt = rbg + E;                    // [E] true totals (tot is padded, then scanned)
   __shared__ int32_t wave_sums[kPlanWaves];
+  __shared__ int s_stalled;
 
   const int tid = threadIdx.x;
   const int lane = lane_id();
   const int wave = tid / kWave;
   const int b = blockIdx.x;
+  if (tid == 0) s_stalled = 0;  // read only after the barrier below
   // This launch's descriptor tag: one more than the launches completed on
   // this workspace (kept in the workspace, so replays of a captured graph
   // get fresh tags too; 0 never tags a descriptor).
@@ -565,8 +577,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
       hist[w * E + e] = run;
       run += v;
     }
-    __hip_atomic_store(&desc[(int64_t)b * E + e], ((uint64_t)epoch << 32) | (uint32_t)run,
-                       __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (b != withhold_tile)  // withhold_tile >= 0 only to test the stall path
+      __hip_atomic_store(&desc[(int64_t)b * E + e], ((uint64_t)epoch << 32) | (uint32_t)run,
+                         __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 
   // Read every tile's counts.  Thread (e, h) sums tiles p = h, h + tpe, ...
@@ -577,6 +590,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
   const int first_g = g * tiles_per_rank, last_g = first_g + tiles_per_rank - 1;
   const int tpe = E >= kPlanThreads ? 1 : kPlanThreads / E;
   const int n_exp = E > kPlanThreads ? 2 : 1;
+  int budget = spin_limit;
   if (tid < tpe * E || E > kPlanThreads) {
     for (int xe = 0; xe < n_exp; ++xe) {
       const int e = E > kPlanThreads ? tid + xe * kPlanThreads : tid % E;
@@ -597,7 +611,7 @@ __global__ __launch_bounds__(kPlanThreads) void plan_fused_kernel(
           const int p = p0 + u * tpe;
           if (p >= ntiles) continue;
           int v = (uint32_t)(raw[u] >> 32) == epoch ? (int)(raw[u] & 0xffffffffull)
-                                                     : (int)wait_descriptor(&desc[(int64_t)p * E + e], epoch);
+                                                     : (int)wait_descriptor(&desc[(int64_t)p * E + e], epoch, budget, &s_stalled);
           a_tot += v;
           if (p < b) a_pre += v;
           if (p < first_s) a_rbase += v;

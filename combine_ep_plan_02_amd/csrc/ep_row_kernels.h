@@ -759,86 +759,152 @@ __global__ __launch_bounds__(kRowThreads) void copy_splits_kernel(
   }
 }
 
-// The plan and the data move of the 1-D all-to-all in one launch.  Same grid
-// as copy_splits_kernel; each workgroup first derives its own chunk's plan
-// entries from the send matrix in_splits[p][r] (W*W values, read through
-// the cache by every workgroup): its threads split the matrix and reduce
-//   src  = sum_{r' < r} in_splits[p][r']          (row in p's input)
-//   dst  = sum_{p' < p} in_splits[p'][r]          (row in r's output)
-//   base = sum_{r' < r} sum_{p'} in_splits[p'][r'] (rank_offsets[r])
-// and the total (rank_offsets[W]).  The y == 0 workgroup of each chunk
-// writes the chunk's plan entries to the optional outputs.
+// The plan and the data move of the 1-D all-to-all in one launch, balanced
+// by rows.  The send matrix in_splits[p][r] (sender p, receiver r; W*W
+// values) is staged in LDS by every workgroup, which derives from it
+//   rank_offsets[r] = sum_{r' < r} sum_p in_splits[p][r']   (receiver bases)
+// and checks that every entry is >= 0 and every sender's row sums to at most
+// R.  Such a matrix places every chunk inside the buffers, and the output is
+// the W*R-row space [0, rank_offsets[W]) covered by the chunks back to back,
+// so the work is split by output rows: workgroup b copies rows
+// [b*RPB, (b+1)*RPB), each wave a contiguous run of RPW rows.  A wave finds
+// the chunk of its first row (and again whenever it crosses into the next):
+//   r = number of receivers r' >= 1 with rank_offsets[r'] <= o,
+//   p = number of senders whose inclusive prefix of column r is <= o - rank_offsets[r],
+//   src = sum_{r' < r} in_splits[p][r'] + (o - start of (r, p)'s chunk),
+// from lane-parallel scans over the W <= 64 lanes of the wave.  Every chunk
+// thus gets waves in proportion to its rows (a fixed number of workgroups
+// per chunk leaves the largest chunks' waves copying long after the rest).
+// Any other matrix (a negative entry, a row summing past R) takes the
+// chunk-by-chunk form: each chunk's offsets are derived as above from the
+// prefix sums, a chunk reaching outside the buffers is skipped and raises
+// kErrSplits, and the workgroups take chunks in turn.  Workgroup b < W
+// also writes receiver b's row of the plan (each output may be null).
+constexpr int kA2ARowsPerWaveBytes = 16384;  // bytes a wave copies per run
+
+template <int U, bool NTL, bool NTS>
+__device__ __forceinline__ void copy_row(const u32x4* __restrict__ s, u32x4* __restrict__ d, int64_t Vr, int lane) {
+  for (int64_t v0 = 0; v0 < Vr; v0 += kWave * U) {
+    u32x4 t[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t idx = v0 + u * kWave + lane;
+      if (idx < Vr) t[u] = ld<NTL>(s + idx);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t idx = v0 + u * kWave + lane;
+      if (idx < Vr) st<NTS>(d + idx, t[u]);
+    }
+  }
+}
+
 template <int U, bool NTL, bool NTS>
 __global__ __launch_bounds__(kRowThreads) void all_to_all_splits_kernel(
     const u32x4* __restrict__ in, u32x4* __restrict__ out, const int64_t* __restrict__ in_splits,
     int64_t* __restrict__ src_offsets, int64_t* __restrict__ out_splits, int64_t* __restrict__ dst_offsets,
-    int64_t* __restrict__ rank_offsets, int W, int64_t R, int64_t Vr) {
-  __shared__ int64_t part[4][kRowThreads / kWave];
-  const int q = blockIdx.x;
-  const int r = q / W, p = q - r * W;
+    int64_t* __restrict__ rank_offsets, int W, int64_t R, int64_t Vr, int64_t rows_per_wave,
+    int64_t n_ranges) {
+  extern __shared__ int64_t a2a_lds[];
+  int64_t* cnt = a2a_lds;              // [W][W] send matrix, sender-major
+  int64_t* base = a2a_lds + W * W;     // [W + 1] receiver bases (rank_offsets)
+  __shared__ int s_bad;
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  int64_t a_src = 0, a_dst = 0, a_base = 0, a_tot = 0;
-  for (int e = tid; e < W * W; e += kRowThreads) {
-    const int pp = e / W, rr = e - pp * W;
-    const int64_t v = in_splits[e];
-    if (pp == p && rr < r) a_src += v;
-    if (rr == r && pp < p) a_dst += v;
-    if (rr < r) a_base += v;
-    a_tot += v;
-  }
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) {
-    a_src += __shfl_xor(a_src, off, kWave);
-    a_dst += __shfl_xor(a_dst, off, kWave);
-    a_base += __shfl_xor(a_base, off, kWave);
-    a_tot += __shfl_xor(a_tot, off, kWave);
-  }
-  if (lane == 0) {
-    part[0][wave] = a_src;
-    part[1][wave] = a_dst;
-    part[2][wave] = a_base;
-    part[3][wave] = a_tot;
+  if (tid == 0) s_bad = 0;
+  for (int e = tid; e < W * W; e += kRowThreads) cnt[e] = in_splits[e];
+  __syncthreads();
+  if (tid < W) {  // receiver tid's column sum; sender tid's row check
+    int64_t col = 0, row = 0;
+    bool neg = false;
+    for (int q = 0; q < W; ++q) {
+      const int64_t c = cnt[(int64_t)q * W + tid], rv = cnt[(int64_t)tid * W + q];
+      col += c;
+      row += rv;
+      neg |= c < 0;
+    }
+    base[tid + 1] = col;
+    if (neg || row > R) s_bad = 1;
   }
   __syncthreads();
-  int64_t src = 0, dsub = 0, base = 0, tot = 0;
-#pragma unroll
-  for (int w = 0; w < kRowThreads / kWave; ++w) {
-    src += part[0][w];
-    dsub += part[1][w];
-    base += part[2][w];
-    tot += part[3][w];
+  if (tid == 0) {
+    int64_t run = 0;
+    base[0] = 0;
+    for (int r = 0; r < W; ++r) {
+      run += base[r + 1];
+      base[r + 1] = run;
+    }
   }
-  const int64_t n = in_splits[(int64_t)p * W + r];
-  if (blockIdx.y == 0 && tid == 0) {
-    if (out_splits) out_splits[q] = n;
-    if (src_offsets) src_offsets[q] = src;
-    if (dst_offsets) dst_offsets[q] = dsub;
-    if (rank_offsets && p == 0) rank_offsets[r] = base;
-    if (rank_offsets && q == 0) rank_offsets[W] = tot;
+  __syncthreads();
+
+  // Receiver b's row of the plan.
+  for (int r = blockIdx.x; r < W; r += gridDim.x) {
+    for (int p = tid; p < W; p += kRowThreads) {
+      int64_t so = 0, dsub = 0;
+      for (int q = 0; q < r; ++q) so += cnt[(int64_t)p * W + q];
+      for (int q = 0; q < p; ++q) dsub += cnt[(int64_t)q * W + r];
+      const int64_t j = (int64_t)r * W + p;
+      if (out_splits) out_splits[j] = cnt[(int64_t)p * W + r];
+      if (src_offsets) src_offsets[j] = so;
+      if (dst_offsets) dst_offsets[j] = dsub;
+    }
+    if (rank_offsets && tid == 0) rank_offsets[r] = base[r];
   }
-  const int64_t dst = base + dsub;
-  if (n == 0) return;
-  if (n < 0 || src < 0 || src + n > R || dst < 0 || dst + n > (int64_t)W * R) {
-    if (blockIdx.y == 0 && tid == 0) raise_device_error(kErrSplits);
-    return;
-  }
-  const int64_t step = (int64_t)gridDim.y * kTokensPerBlock;
-  for (int64_t i = (int64_t)blockIdx.y * kTokensPerBlock + wave; i < n; i += step) {
-    const u32x4* s = in + ((int64_t)p * R + src + i) * Vr;
-    u32x4* d = out + (dst + i) * Vr;
-    for (int64_t v0 = 0; v0 < Vr; v0 += kWave * U) {
-      u32x4 t[U];
+  if (rank_offsets && blockIdx.x == 0 && tid == 0) rank_offsets[W] = base[W];
+  if (R == 0) return;
+
+  if (!s_bad) {
+    const int64_t total = base[W];
+    for (int64_t g = blockIdx.x; g < n_ranges; g += gridDim.x) {
+      int64_t o = (g * (kRowThreads / kWave) + wave) * rows_per_wave;
+      const int64_t o_end = min(o + rows_per_wave, total);
+      int64_t chunk_end = -1, shift = 0;  // input row of output row o: o + shift
+      for (; o < o_end; ++o) {
+        if (o >= chunk_end) {
+          // receiver of row o
+          const bool past = lane >= 1 && lane <= W && base[lane] <= o;
+          const int r = __popcll(ballot(past));
+          const int64_t orr = o - base[r];
+          // sender: inclusive prefix of column r over the lanes
+          const int64_t c = lane < W ? cnt[(int64_t)lane * W + r] : 0;
+          int64_t incl = c;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t idx = v0 + u * kWave + lane;
-        if (idx < Vr) t[u] = ld<NTL>(s + idx);
-      }
+          for (int off = 1; off < kWave; off <<= 1) {
+            const int64_t v = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += v;
+          }
+          const int p = __popcll(ballot(lane < W && incl <= orr));
+          const int64_t incl_p = __shfl(incl, p, kWave);
+          const int64_t n_p = __shfl(c, p, kWave);
+          // rows sender p sends to receivers before r
+          int64_t so = lane < r ? cnt[(int64_t)p * W + lane] : 0;
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t idx = v0 + u * kWave + lane;
-        if (idx < Vr) st<NTS>(d + idx, t[u]);
+          for (int off = kWave / 2; off > 0; off >>= 1) so += __shfl_xor(so, off, kWave);
+          const int64_t chunk_start = base[r] + incl_p - n_p;
+          chunk_end = base[r] + incl_p;
+          shift = (int64_t)p * R + so - chunk_start;
+        }
+        copy_row<U, NTL, NTS>(in + (o + shift) * Vr, out + o * Vr, Vr, lane);
       }
     }
+    return;
+  }
+
+  // Chunk by chunk (a matrix that does not place every chunk inside the
+  // buffers): the checks and skips of ep_dispatch_splits.
+  for (int q = blockIdx.x; q < W * W; q += gridDim.x) {
+    const int r = q / W, p = q - r * W;
+    const int64_t n = cnt[(int64_t)p * W + r];
+    if (n == 0) continue;
+    int64_t so = 0, dsub = 0;
+    for (int j = 0; j < r; ++j) so += cnt[(int64_t)p * W + j];
+    for (int j = 0; j < p; ++j) dsub += cnt[(int64_t)j * W + r];
+    const int64_t dst = base[r] + dsub;
+    if (n < 0 || so < 0 || so + n > R || dst < 0 || dst + n > (int64_t)W * R) {
+      if (tid == 0) raise_device_error(kErrSplits);
+      continue;
+    }
+    for (int64_t i = wave; i < n; i += kRowThreads / kWave)
+      copy_row<U, NTL, NTS>(in + ((int64_t)p * R + so + i) * Vr, out + (dst + i) * Vr, Vr, lane);
   }
 }
 

@@ -132,9 +132,24 @@ typedef struct {
     int32_t major_align;
     int32_t pad_empty_experts;
     int32_t expert_token_nums_type;
-    int32_t reserved;
+    int32_t flags;              /* EP_PLAN_* bits, 0 for none */
     int64_t *expert_token_nums;
 } ep_plan_opts_t;
+
+/* ep_plan_opts_t.flags.
+ * EP_PLAN_LOOKBACK: never take the one-launch plan; the plan then waits
+ *   only on tiles that are already running, whatever else the device runs
+ *   (the ExchangePlan of the PyTorch compare view never depends on its
+ *   blocks being resident together either).  For callers that keep other
+ *   kernels that may fill the device running beside the plan.
+ * EP_PLAN_TEST_STALL: a test hook for the stall path of the one-launch plan:
+ *   the last tile withholds its counts and every wait's budget is a few
+ *   hundred polls, so every tile gives up, EP_DEVERR_PLAN_STALL is raised and
+ *   the plan is invalid; every kernel still exits normally and the next call
+ *   on the same workspace is correct.  No effect when the plan takes the
+ *   look-back path. */
+#define EP_PLAN_LOOKBACK 1
+#define EP_PLAN_TEST_STALL 0x40000000
 
 #define EP_MAX_ALIGN 4096
 
@@ -176,12 +191,18 @@ int ep_workspace_init(void *workspace, size_t ws_bytes, void *stream);
  * The result is deterministic and identical to the serial definition.
  * T == 0 writes the all-zero plan.  The workspace (size from
  * ep_workspace_size, initialised once with ep_workspace_init) must not be
- * used by two calls in flight at the same time.
- * When all of its tiles fit on the device at once the plan is one launch
- * whose tiles exchange counts while running; every wait is bounded, so a
- * kernel on another stream that keeps the compute units busy for about a
- * second makes the plan give up with EP_DEVERR_PLAN_STALL rather than hang.
- * Larger grids use a look-back that only waits on tiles already running. */
+ * used by two calls in flight at the same time.  Its regions are laid out
+ * from (T, K, E, W): every call leaves it ready for the next call with the
+ * same dimensions; before a call with other dimensions, initialise it
+ * again.
+ * When its tiles fill at most half of what the device runs at once (and
+ * opts does not ask for EP_PLAN_LOOKBACK) the plan is one launch whose
+ * tiles exchange counts while running.  Every wait is bounded: if kernels
+ * on other streams keep some tiles from being scheduled for about a second,
+ * each waiting tile gives up within that one budget and the plan ends with
+ * EP_DEVERR_PLAN_STALL rather than hanging.  Larger grids, and
+ * EP_PLAN_LOOKBACK, use a look-back that only waits on tiles already
+ * running. */
 int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t *topk_ids,
             const uint8_t *active, const ep_plan_opts_t *opts, const ep_plan_t *plan,
             void *workspace, size_t ws_bytes, void *stream);

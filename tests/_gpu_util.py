@@ -50,8 +50,8 @@ class GpuPath:
         self.ws = ep.alloc_workspace(T, K, E, W)
         self.plan = ep.alloc_plan(T, K, E, W, with_occ=with_occ)
 
-    def run_plan(self):
-        ep.ep_plan(self.ids, self.E, self.W, self.plan, self.ws, self.active)
+    def run_plan(self, flags=0):
+        ep.ep_plan(self.ids, self.E, self.W, self.plan, self.ws, self.active, flags=flags)
         return self.plan
 
     def plan_host(self):

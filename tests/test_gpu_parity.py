@@ -56,7 +56,9 @@ PLAN_CASES = [
     (20000, 7, 14, 2, 0.2, 8, "dup"),       # 2 ranks x 35 tiles
     (8448, 16, 1024, 2, 0.1, 9, "distinct"),  # 66 tiles x 1024 experts: look-back path
     (8192, 16, 1024, 2, 0.1, 11, "distinct"),  # 64 x 1024 = 65536 descriptors: fused, at its limit
-    (131072, 8, 64, 8, 0.0, 10, "dup"),     # 512 tiles: fused with two tiles per CU (all of MI355X)
+    (65536, 8, 64, 8, 0.0, 14, "dup"),      # 256 tiles: fused, at half of what MI355X runs at once
+    (65792, 8, 64, 8, 0.0, 15, "dup"),      # 257 tiles: look-back path
+    (131072, 8, 64, 8, 0.0, 10, "dup"),     # 512 tiles (all of MI355X at once): look-back path
     (131584, 8, 64, 8, 0.0, 13, "dup"),     # 520 tiles, past what runs at once: look-back path
     (131072, 8, 256, 8, 0.0, 12, "dup"),    # 512 tiles x 256 experts: look-back, walking windows
 ]
@@ -409,6 +411,47 @@ def test_fused_splits_bad_matrix_is_flagged():
     want_out, err = oracle.a2a_copy(inp, want, fill=-1)
     assert err == oracle.DEVERR_SPLITS
     assert (host(out) == want_out).all()
+
+
+def test_fused_splits_negative_entry_is_flagged():
+    """A negative send count: that chunk is skipped and flagged, every other
+    chunk moves where the prefix sums (negative entry included) put it, as
+    the oracle's copy of the same plan does."""
+    say("fused splits, negative send count")
+    send = np.array([[2, 1], [1, -1]], np.int64)
+    inp = np.arange(2 * 4 * 8, dtype=np.int32).reshape(2, 4, 8)
+    sp, out = run_fused_splits(send, inp)
+    assert ep.ep_device_error() == ep.EP_DEVERR_SPLITS
+    want = oracle.a2a_plan(send)
+    for f in ("src_offsets", "out_splits", "dst_offsets", "rank_offsets"):
+        assert (host(getattr(sp, f)) == getattr(want, f)).all(), f
+    want_out, err = oracle.a2a_copy(inp, want, fill=-1)
+    assert err == oracle.DEVERR_SPLITS
+    assert (host(out) == want_out).all()
+
+
+@pytest.mark.parametrize("R,row_values", [(3000, 8), (700, 2056)])
+def test_fused_splits_rows_cross_runs(R, row_values):
+    """Runs of rows that cross many chunk boundaries (short rows: one wave's
+    run spans several chunks) and long rows (a run of one row, several
+    16-byte vectors per lane), with W = 64 and empty receivers."""
+    rng = np.random.default_rng(R)
+    W = 64
+    send = np.zeros((W, W), np.int64)
+    for p in range(W):
+        cuts = np.sort(rng.integers(0, R + 1, W - 1))
+        send[p] = np.diff(np.concatenate([[0], cuts, [R]]))
+    send[:, 5] = 0                          # receiver 5 gets nothing
+    send[:, 6] += send[:, 5]
+    send[7, :] = 0                          # sender 7 sends nothing
+    inp = rng.integers(0, 1 << 16, size=(W, R, row_values)).astype(np.uint16)
+    say("fused splits W 64 R", R, "row values", row_values)
+    sp, out = run_fused_splits(send, inp)
+    want = oracle.a2a_plan(send)
+    want_out, err = oracle.a2a_copy(inp, want, fill=0xFFFF)
+    assert err == 0
+    assert (host(out, np.uint16) == want_out).all()
+    assert ep.ep_device_error() == 0
 
 
 def test_fused_splits_all_to_all_workload_full():
