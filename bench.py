@@ -1,6 +1,11 @@
 """Benchmark: MoE expert-parallel dispatch + combine on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload 2] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload N] [--gpus 1]
+
+With no --workload, the line is the T=16384, H=7168, E=256, K=8, W=32 step
+(25% of tokens masked, per-token fp8 dispatch, bf16 combine) with the
+T=8192, H=7168, E=256, K=8, W=16 Zipf step's whole record nested in it
+("also_measured"): the two largest MoE workloads.
 
 One step is the whole hot path over one batch of resident synthetic input:
 ep_plan (split counts, scans, exchange plan, stable positions) -> ep_dispatch
@@ -96,9 +101,11 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=20)
-    ap.add_argument("--workload", type=int, default=2, choices=[0, 1, 2, 3, 4],
-                    help="index of the workload (2: T=8192 H=7168 E=256 K=8 W=16 Zipf; "
-                         "0: the T=64 latency case)")
+    ap.add_argument("--workload", type=int, default=None, choices=[0, 1, 2, 3, 4],
+                    help="index of the workload to time alone (default: 4, T=16384 H=7168 E=256 "
+                         "K=8 W=32 with 25%% masked tokens and fp8 dispatch, as the headline, with "
+                         "2, T=8192 H=7168 E=256 K=8 W=16 Zipf, measured after it and nested in "
+                         "the same line; 0: the T=64 latency case)")
     ap.add_argument("--graph", action="store_true",
                     help="capture one step into a HIP graph and time its replays (no host "
                          "launch cost per kernel; what a launch-bound small step needs)")
@@ -171,6 +178,10 @@ class MoEBench:
     def plan_step(self):
         self.ep.ep_plan(self.ids, self.cfg.E, self.cfg.W, self.plan, self.ws, self.active)
 
+    def plan_lookback_step(self):
+        self.ep.ep_plan(self.ids, self.cfg.E, self.cfg.W, self.plan, self.ws, self.active,
+                        flags=self.ep.EP_PLAN_LOOKBACK)
+
     def dispatch_step(self):
         self.ep.ep_dispatch(self.x, self.plan.pos, self.ex, self.scales, out_dtype=self.out_dtype)
 
@@ -206,10 +217,12 @@ class MoEBench:
         return [("ep_plan", self.plan_step), ("ep_dispatch", self.dispatch_step), last]
 
     def extra_phases(self):
-        """Kernels timed beside the step: the quantisation variants (smoothed
-        fp8 dispatch, combine of fp8 expert rows, int8 dispatch and combine of
-        int8 rows) and, with the tail, the unfused tail pair."""
-        ph = [("ep_dispatch_smooth", self.dispatch_smooth_step),
+        """Kernels timed beside the step: the plan forced onto its look-back
+        path, the quantisation variants (smoothed fp8 dispatch, combine of fp8
+        expert rows, int8 dispatch and combine of int8 rows) and, with the
+        tail, the unfused tail pair."""
+        ph = [("ep_plan_lookback", self.plan_lookback_step),
+              ("ep_dispatch_smooth", self.dispatch_smooth_step),
               ("ep_combine_quant", self.combine_quant_step),
               ("ep_dispatch_int8", self.dispatch_int8_step),
               ("ep_combine_quant_int8", self.combine_int8_step)]
@@ -237,7 +250,7 @@ class MoEBench:
         # row scales out, ids + pos; fp8 combine: codes + row scales in, out rows
         smooth_b = self.live_tokens * row_in + c.E * c.H * 4 + N * (c.H + 4) + tk * 4 * 2
         combq_b = N * (c.H + 4) + c.T * 2 * c.H + tk * 4 * 2
-        return {"ep_plan": plan_b, "ep_dispatch": disp_b, "ep_combine": comb_b,
+        return {"ep_plan": plan_b, "ep_plan_lookback": plan_b, "ep_dispatch": disp_b, "ep_combine": comb_b,
                 "ep_combine_add_rmsnorm": tail_b, "ep_add_rmsnorm": addn_b,
                 "ep_dispatch_smooth": smooth_b, "ep_combine_quant": combq_b,
                 "ep_dispatch_int8": self.live_tokens * row_in + N * (c.H + 4) + tk * 4,
@@ -394,8 +407,22 @@ def main():
     import combine_ep_plan_02_amd as ep
     import workloads
 
-    cfg = workloads.WORKLOADS[args.workload]
-    if args.workload == 3:
+    if args.workload is not None:
+        rec = measure(args.workload, args, torch, ep, workloads)
+    else:
+        # The two largest MoE workloads: the T=16384 fp8 one as the headline,
+        # the T=8192 Zipf one measured after it, in full, and nested in the
+        # same line.
+        rec = measure(4, args, torch, ep, workloads)
+        torch.cuda.empty_cache()
+        rec["also_measured"] = [measure(2, args, torch, ep, workloads)]
+    print(json.dumps(rec), flush=True)
+
+
+def measure(workload, args, torch, ep, workloads):
+    """Times one workload; returns its JSON record."""
+    cfg = workloads.WORKLOADS[workload]
+    if workload == 3:
         bench = SplitsBench(cfg, torch, ep, workloads)
     else:
         bench = MoEBench(cfg, torch, ep, workloads, tail=args.tail)
@@ -507,6 +534,28 @@ def main():
         phase_ms[name] = a.elapsed_time(b) / args.steps
     eager_step()  # leave the buffers in the state of one whole step
     torch.cuda.synchronize()
+
+    # Cold launches of each step kernel: the Infinity Cache refilled with
+    # clean lines of an unrelated 512 MB buffer before every launch, as for
+    # the cold steps, one event pair around each launch.
+    log("[bench] cold per-phase timing")
+    scratch = torch.ones(128 << 20, dtype=torch.int32, device="cuda")
+    phase_cold_ms = {}
+    for name, fn in phases:
+        ev = []
+        for _ in range(args.steps):
+            scratch.sum()
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            ev.append((a, b))
+        torch.cuda.synchronize()
+        phase_cold_ms[name] = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    del scratch
+    eager_step()
+    torch.cuda.synchronize()
     assert ep.ep_device_error() == 0
 
     N = bench.n_rows()
@@ -524,7 +573,7 @@ def main():
     rec = {
         "metric": METRIC,
         "value": tokens / (ms_per_step * 1e-3),
-        "unit": "tokens/s" if args.workload != 3 else "rows/s",
+        "unit": "tokens/s" if workload != 3 else "rows/s",
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": ms_per_step,
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
@@ -536,6 +585,10 @@ def main():
         "cold_step_us": spread(cold_list),
         "cold_hbm_gbps": step_bytes / (cold_ms * 1e-3) / 1e9,
         "hbm_frac_of_peak": step_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "cold_hbm_frac_of_peak": step_bytes / (cold_ms * 1e-3) / 1e9 / HBM_PEAK_GBPS,
+        "cache_note": "warm steps (value, ms_per_step, hbm_*) reuse one input batch, whose x rows "
+                      "the 256 MB Infinity Cache largely keeps between steps; cold_* figures "
+                      "refill that cache with an unrelated buffer before every step or launch",
         "algorithmic_bytes_per_step": step_bytes,
         "rows_N": N,
         "source_sha256": source_digest(),
@@ -544,13 +597,20 @@ def main():
                           if step_phase_ms is not None else None),
         "phase_gbps": {k: bpp[k] / (phase_ms[k] * 1e-3) / 1e9 for k in phase_ms},
         "phase_algorithmic_bytes": {k: bpp[k] for k in phase_ms},
-        "phase_traffic_bytes": {k: measured_traffic(args.workload, k) for k in phase_ms},
+        "phase_cold_us": {k: v * 1e3 for k, v in phase_cold_ms.items()},
+        "phase_fabric_bytes": {k: measured_traffic(workload, k) for k in phase_ms},
+        "fabric_bytes_note": "rocprofv3 FETCH_SIZE + WRITE_SIZE per launch (L2 fills and "
+                             "write-backs over the fabric, Infinity Cache hits included), "
+                             "scaled by a plain copy's counts; null for other library sources",
         "step_phases": step_names,
         "roofline": {"kernel": dominant, "bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBPS,
                      "unit": "GB/s", "frac": ach / HBM_PEAK_GBPS,
-                     "traffic": measured_traffic(args.workload, dominant),
+                     "traffic": measured_traffic(workload, dominant),
                      "algorithmic_bytes_per_launch": bpp[dominant],
                      "duration_us": phase_ms[dominant] * 1e3,
+                     "cold_duration_us": phase_cold_ms[dominant] * 1e3,
+                     "cold_achieved": bpp[dominant] / (phase_cold_ms[dominant] * 1e-3) / 1e9,
+                     "cold_frac": bpp[dominant] / (phase_cold_ms[dominant] * 1e-3) / 1e9 / HBM_PEAK_GBPS,
                      "in_step_event_us": (step_phase_ms[dominant] * 1e3
                                           if step_phase_ms is not None else None)},
     }
@@ -566,7 +626,8 @@ def main():
             rec["cpu_baseline"] = bench.cpu_baseline(args.cpu_reps) | host_cpu() | {"pinned_core": min(allowed)}
         finally:
             os.sched_setaffinity(0, allowed)
-    print(json.dumps(rec), flush=True)
+    del bench
+    return rec
 
 
 if __name__ == "__main__":
