@@ -158,15 +158,23 @@ __device__ __forceinline__ u32x4 quantize16f(const float* f, float scale) {
 // x / scale for one row's scale, correctly rounded, with the reciprocal
 // refined once per row.  The element step is the compiler's IEEE fp32
 // divide sequence without its operand scaling: q = n r, then two corrections
-// q += (n - s q) r by fused multiply-adds.  The scaling of that sequence only
-// acts on extreme exponents, so the fast form is taken for scales in
-// [2^-60, 2^60]; there every quotient of at least 2^-11 in magnitude has
-// normal operands and exact remainders, and smaller quotients give codes of
-// zero.  The remainder is formed negated, e = s q - n, and subtracted,
-// q - e r: the same roundings (round to nearest is symmetric), and a zero n
-// keeps its sign through both corrections (with e = n - s q a -0 would come
-// back as +0).  Other scales (zero, subnormal, huge, infinite, NaN) take the
-// plain division.
+// q += (n - s q) r by fused multiply-adds.  That correction rounds correctly
+// when r is the correctly rounded 1/s (Markstein's theorem), so r is made
+// exactly that: one Newton step r0 + r0 (1 - s r0) from v_rcp_f32's result
+// (specified to 1 ulp) gives it for every scale except those whose mantissa
+// is all ones, s = 2^k (2 - 2^-23); there 1/s = 2^-k-1 (1 + 2^-24 + 2^-48 +
+// ...), just above the midpoint of 2^-k-1 and its successor, and the step
+// can stop on the midpoint and round down, so r is set to that successor
+// directly.  (Checked on the host over every mantissa and every r0 within an
+// ulp, and for the quotients at every code's rounding boundaries.)  The
+// scaling of the compiler's sequence only acts on extreme exponents, so the
+// fast form is taken for scales in [2^-60, 2^60]; there every quotient of at
+// least 2^-11 in magnitude has normal operands and exact remainders, and
+// smaller quotients give codes of zero.  The remainder is formed negated,
+// e = s q - n, and subtracted, q - e r: the same roundings (round to nearest
+// is symmetric), and a zero n keeps its sign through both corrections (with
+// e = n - s q a -0 would come back as +0).  Other scales (zero, subnormal,
+// huge, infinite, NaN) take the plain division.
 struct RowDiv {
   float s, r;
   bool fast;
@@ -178,6 +186,9 @@ __device__ __forceinline__ RowDiv row_div(float scale) {
   d.fast = d.s >= 0x1p-60f && d.s <= 0x1p60f;
   const float r0 = __builtin_amdgcn_rcpf(d.s);
   d.r = __builtin_fmaf(__builtin_fmaf(-d.s, r0, 1.0f), r0, r0);
+  const uint32_t sb = __float_as_uint(d.s);
+  if ((sb & 0x7fffffu) == 0x7fffffu)  // all-ones mantissa: 1/s rounds to 2^-k-1 (1 + 2^-23)
+    d.r = __uint_as_float(((253u - ((sb >> 23) & 0xffu)) << 23) | 1u);
   return d;
 }
 
