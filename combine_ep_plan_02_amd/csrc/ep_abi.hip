@@ -424,10 +424,11 @@ EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, co
   const size_t cap = reachable_rows(cap_rows);
   const size_t eb = cap * H * (quant ? 1 : 2);
   const size_t sb = quant ? cap * 4 : 0;
-  if (overlap(expand_x, eb, x, xb) || overlap(expand_x, eb, pos, pb))
+  const size_t wtb = weights ? pb : 0;  // weights [T][K] fp32, as large as pos
+  if (overlap(expand_x, eb, x, xb) || overlap(expand_x, eb, pos, pb) || overlap(expand_x, eb, weights, wtb))
     return fail(EP_ERR_INVALID, "expand_x overlaps an input");
   if (quant && (overlap(expand_scales, sb, x, xb) || overlap(expand_scales, sb, pos, pb) ||
-              overlap(expand_scales, sb, expand_x, eb)))
+              overlap(expand_scales, sb, weights, wtb) || overlap(expand_scales, sb, expand_x, eb)))
     return fail(EP_ERR_INVALID, "expand_scales overlaps another buffer");
   const size_t wb = expand_weights ? cap * 4 : 0;
   if (expand_weights &&

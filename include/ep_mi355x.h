@@ -335,14 +335,22 @@ int ep_all_to_all_splits(int32_t W, int64_t R, int64_t stride_bytes, const int64
                          const void *in, void *out, int64_t *src_offsets, int64_t *out_splits,
                          int64_t *dst_offsets, int64_t *rank_offsets, void *stream);
 
-/* Thread-local description of the last non-OK status ("" if none). */
+/* Thread-local description of the last non-OK status ("" if none).  The
+ * status carries the class, as the return codes of the CANN
+ * "aclnnMoeDistributeDispatchV2" Returns table do (null pointers,
+ * unsupported data types, unsupported shapes or parameter values); this
+ * text names the failing check and its values. */
 const char *ep_last_error(void);
 
 /* Synchronises `stream`, then returns in *code the device error bits
  * (EP_DEVERR_*) raised on the current device since the previous call, and
  * clears those bits (an atomic AND enqueued on `stream`, then waited for):
  * a bit a kernel on another stream raises meanwhile stays set for the next
- * call. */
+ * call.  The kernels of the PyTorch compare view "ciflow/h100-symm-mem/166772"
+ * check their device-side preconditions with in-kernel asserts, which abort
+ * (CUDA_KERNEL_ASSERT in exchangeSplitAndOffset and allToAllGet); here a
+ * data error seen on the device drops the offending copy or chunk, raises a
+ * bit, and the caller reads the bits with this call. */
 int ep_device_error(void *stream, int32_t *code);
 
 #ifdef __cplusplus

@@ -155,6 +155,11 @@ def test_dispatch_rejections(ep):
     assert d(64, 2, 128, X, P, ep.EP_BF16, EX, None, None, EW, 128, None) == ep.EP_ERR_NULLPTR
     assert d(64, 2, 128, X, P, ep.EP_BF16, EX, None, WT, EW + 2, 128, None) == ep.EP_ERR_INVALID
     assert d(64, 2, 128, X, P, ep.EP_BF16, EX, None, WT, EX + 64, 128, None) == ep.EP_ERR_INVALID
+    # an output over the gate weights (an input the kernels read)
+    assert d(64, 2, 128, X, P, ep.EP_BF16, WT - 256, None, WT, EW, 128, None) == ep.EP_ERR_INVALID
+    assert "expand_x overlaps" in ep.lib.ep_last_error().decode()
+    assert d(64, 2, 128, X, P, ep.EP_FP8_E4M3FN, EX, WT + 128, WT, EW, 128, None) == ep.EP_ERR_INVALID
+    assert "expand_scales overlaps" in ep.lib.ep_last_error().decode()
     # empty input: OK, nothing enqueued, pointers may be NULL
     assert d(0, 2, 128, None, None, ep.EP_BF16, None, None, None, None, 0, None) == ep.EP_OK
 
