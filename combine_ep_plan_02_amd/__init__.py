@@ -44,7 +44,7 @@ _STATUS_NAMES = {1: "EP_ERR_NULLPTR", 2: "EP_ERR_INVALID", 3: "EP_ERR_UNSUPPORTE
                  4: "EP_ERR_WORKSPACE", 5: "EP_ERR_HIP"}
 
 EXPORTED = ("ep_supported", "ep_workspace_size", "ep_workspace_init", "ep_expand_rows_bound",
-            "ep_plan", "ep_dispatch", "ep_dispatch_smooth", "ep_combine", "ep_combine_quant",
+            "ep_plan", "ep_plan_noalloc", "ep_dispatch", "ep_dispatch_smooth", "ep_combine", "ep_combine_quant",
             "ep_combine_add_rmsnorm", "ep_add_rmsnorm",
             "ep_plan_splits", "ep_dispatch_splits", "ep_all_to_all_splits", "ep_last_error",
             "ep_device_error")
@@ -82,6 +82,8 @@ def _load() -> ctypes.CDLL:
         "ep_expand_rows_bound": ([i32, i32, i32, i32, i32], i64),
         "ep_plan": ([i32, i32, i32, i32, P, P, ctypes.POINTER(_PlanOpts), ctypes.POINTER(_PlanT), P,
                      sz, P], ctypes.c_int),
+        "ep_plan_noalloc": ([i32, i32, i32, i32, P, P, ctypes.POINTER(_PlanOpts), ctypes.POINTER(_PlanT),
+                             P], ctypes.c_int),
         "ep_dispatch": ([i32, i32, i32, P, P, i32, P, P, P, P, i64, P], ctypes.c_int),
         "ep_dispatch_smooth": ([i32, i32, i32, i32, P, P, P, P, i32, P, P, i64, P], ctypes.c_int),
         "ep_combine": ([i32, i32, i32, P, i64, P, P, P, P], ctypes.c_int),
@@ -290,6 +292,24 @@ def ep_plan(topk_ids: torch.Tensor, E: int, W: int, plan: Plan, workspace: torch
                        None if o is None else ctypes.byref(o), ctypes.byref(st),
                        _ptr(workspace, name="workspace"),
                        workspace.numel() * workspace.element_size(), _stream(stream)))
+    return plan
+
+
+def ep_plan_noalloc(topk_ids: torch.Tensor, E: int, W: int, plan: Plan,
+                    active: torch.Tensor | None = None, stream=None, *,
+                    active_copies: torch.Tensor | None = None, major_align: int = 1,
+                    pad_empty_experts: bool = False, expert_token_nums: torch.Tensor | None = None,
+                    expert_token_nums_type: int = 1, flags: int = 0) -> Plan:
+    """ep_plan without a workspace: the library's static per-device array
+    holds the plan's state (calls that overlap on one device race)."""
+    T, K = topk_ids.shape
+    o = _plan_opts(T, K, E, active, active_copies, major_align, pad_empty_experts,
+                   expert_token_nums, expert_token_nums_type, flags)
+    st = plan.as_struct(T, K, E, W)
+    _check(lib.ep_plan_noalloc(T, K, E, W, _ptr(topk_ids, torch.int32, "topk_ids"),
+                               _ptr(active, (torch.uint8, torch.bool), "active"),
+                               None if o is None else ctypes.byref(o), ctypes.byref(st),
+                               _stream(stream)))
     return plan
 
 

@@ -397,6 +397,82 @@ EP_EXPORT int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t*
   return launch_plan(T, K, E, W, topk_ids, active, o, plan, st, fused, (hipStream_t)stream);
 }
 
+// ---------------------------------------------------------------------------
+// The plan without a caller workspace (ep_plan_noalloc): its state lives in
+// `scratch`, one static array per device, laid out at fixed offsets that do
+// not depend on the dimensions, so calls of any size may follow each other:
+//   [0, 256)            header: ticket, epoch, done counter
+//   [256, +16 KiB)      look-back flags, up to kScratchTiles tiles
+//   then 512 KiB        one-launch descriptors (its limit of 65536)
+//   then 1.5 MiB each   look-back aggregates and inclusive prefixes
+// The array starts as zeros (static storage), which is the initial state;
+// every plan returns the flags, ticket and done counter to zero, and the
+// descriptors carry the epoch of the call that wrote them (the epoch only
+// grows), so no call needs the array cleared.  Calls that overlap on one
+// device share the array and race, as two plans on one workspace do.
+// ---------------------------------------------------------------------------
+constexpr size_t kScratchHeader = 256;
+constexpr int kScratchTiles = 4096;
+constexpr size_t kScratchFlags = kScratchHeader;
+constexpr size_t kScratchDesc = kScratchFlags + (size_t)kScratchTiles * 4;
+constexpr size_t kScratchAgg = kScratchDesc + (size_t)ep::kFusedMaxDescriptorsPerTile * 8;
+constexpr size_t kScratchPartBytes = (size_t)3 << 19;  // 1.5 MiB
+constexpr size_t kScratchIncl = kScratchAgg + kScratchPartBytes;
+constexpr size_t kScratchBytes = kScratchIncl + kScratchPartBytes;
+
+__device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// Device address of `scratch` on the current device, looked up once per
+// device with that device current (each GPU holds its own copy); only this
+// address is ever handed to a kernel.
+int scratch_address(uint8_t** out) {
+  static std::mutex mu;
+  static uint8_t* addr[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return fail(EP_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  if (dev < 0 || dev >= kMaxDevices) return fail(EP_ERR_UNSUPPORTED, "device %d beyond %d devices", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lock(mu);
+  if (addr[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || p == nullptr)
+      return fail(EP_ERR_HIP, "hipGetSymbolAddress(scratch) failed: %s", hipGetErrorString(e));
+    addr[dev] = (uint8_t*)p;
+  }
+  *out = addr[dev];
+  return EP_OK;
+}
+
+}  // namespace
+
+EP_EXPORT int ep_plan_noalloc(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t* topk_ids,
+                              const uint8_t* active, const ep_plan_opts_t* opts, const ep_plan_t* plan,
+                              void* stream) {
+  ep_plan_opts_t o;
+  int rc = check_plan_args(T, K, E, W, topk_ids, active, opts, plan, o);
+  if (rc) return rc;
+  const PlanGeometry g = plan_geometry(T, K, W);
+  const bool fused = !(o.flags & EP_PLAN_LOOKBACK) && fused_fits(g.ntiles, E);
+  if (!fused && (g.ntiles > kScratchTiles || (size_t)g.ntiles * E * 4 > kScratchPartBytes))
+    return fail(EP_ERR_UNSUPPORTED,
+                "the plan needs %d tiles x %d experts of look-back state; the static scratch holds %d tiles "
+                "and %zu tile-experts (use ep_plan with a workspace)",
+                g.ntiles, E, kScratchTiles, kScratchPartBytes / 4);
+  rc = check_plan_overlaps(T, K, E, W, topk_ids, active, o, plan, nullptr, 0);
+  if (rc) return rc;
+  uint8_t* base = nullptr;
+  rc = scratch_address(&base);
+  if (rc) return rc;
+  const PlanState st{(uint32_t*)base, (uint32_t*)(base + kScratchFlags), (int32_t*)(base + kScratchAgg),
+                     (int32_t*)(base + kScratchIncl), (uint64_t*)(base + kScratchDesc)};
+  return launch_plan(T, K, E, W, topk_ids, active, o, plan, st, fused, (hipStream_t)stream);
+}
+
 EP_EXPORT int ep_dispatch(int32_t T, int32_t K, int32_t H, const uint16_t* x, const int32_t* pos,
                           int32_t out_dtype, void* expand_x, float* expand_scales, const float* weights,
                           float* expand_weights, int64_t cap_rows, void* stream) {

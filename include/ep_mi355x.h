@@ -207,6 +207,24 @@ int ep_plan(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t *topk_ids,
             const uint8_t *active, const ep_plan_opts_t *opts, const ep_plan_t *plan,
             void *workspace, size_t ws_bytes, void *stream);
 
+/* ep_plan without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  Same arguments, results, options and
+ * errors as ep_plan.  The plan's state lives in a static device array of
+ * the library (about 3.5 MiB per device, held until the process ends),
+ * laid out independently of the dimensions, so calls of any size may follow
+ * each other without initialisation.  Limits: the look-back path (taken
+ * when the one-launch plan does not fit, or with EP_PLAN_LOOKBACK) holds at
+ * most 4096 tiles and 393216 tile-experts (tiles = T*K / 2048, about, never
+ * crossing a source rank), else EP_ERR_UNSUPPORTED; the one-launch plan
+ * always fits.  Every call on a device shares that device's array: calls
+ * that overlap on one device (two streams, two threads) race and must not
+ * be issued; calls on different devices are independent.  Allocates
+ * nothing; its first call on a device looks up the array's address. */
+int ep_plan_noalloc(int32_t T, int32_t K, int32_t E, int32_t W, const int32_t *topk_ids,
+                    const uint8_t *active, const ep_plan_opts_t *opts, const ep_plan_t *plan,
+                    void *stream);
+
 /* Dispatch scatter: for every copy with pos[t][k] >= 0,
  *   EP_BF16:       expand_x[pos][:] = x[t][:]  (bit copy, H bf16 = 2H bytes)
  *   EP_FP8_E4M3FN: per-token dynamic quantisation (CANN quantMode 2):
