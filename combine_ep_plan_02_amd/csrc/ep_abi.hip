@@ -939,15 +939,19 @@ EP_EXPORT int ep_all_to_all_splits(int32_t W, int64_t R, int64_t stride_bytes, c
         return fail(EP_ERR_INVALID, "an output of the all-to-all overlaps another buffer");
     }
   // Work split by output rows (at most W*R of them): a wave copies a run of
-  // rows of about kA2ARowsPerWaveBytes, a workgroup four runs; the grid
-  // loops over the runs when there are more than one launch holds.
+  // rows of about kA2ARowsPerWaveBytes, a workgroup four runs at a time; at
+  // most kA2ABlocks workgroups (four per CU on MI355X), each looping over
+  // runs, so every workgroup's setup (staging the send matrix, its receiver
+  // bases) serves several runs.  Measured on W=8, R=4096, 4 KB rows against
+  // one workgroup per four runs: 41 against 43 us warm, 52 against 56 us
+  // with the Infinity Cache flushed.
   const int64_t Vr = stride_bytes / 16;
   int64_t rows_per_wave = ep::kA2ARowsPerWaveBytes / stride_bytes;
   if (rows_per_wave < 1) rows_per_wave = 1;
   const int64_t rows = (int64_t)W * R;
   const int64_t per_block = rows_per_wave * ep::kTokensPerBlock;
   const int64_t n_ranges = (rows + per_block - 1) / per_block;
-  int64_t blocks = n_ranges < ((int64_t)1 << 20) ? n_ranges : ((int64_t)1 << 20);
+  int64_t blocks = n_ranges < ep::kA2ABlocks ? n_ranges : ep::kA2ABlocks;
   if (blocks < 1) blocks = 1;
   const size_t lds = ((size_t)W * W + W + 1) * sizeof(int64_t);
   hipStream_t s = (hipStream_t)stream;

@@ -777,8 +777,9 @@ __global__ __launch_bounds__(kRowThreads) void copy_splits_kernel(
 // and checks that every entry is >= 0 and every sender's row sums to at most
 // R.  Such a matrix places every chunk inside the buffers, and the output is
 // the W*R-row space [0, rank_offsets[W]) covered by the chunks back to back,
-// so the work is split by output rows: workgroup b copies rows
-// [b*RPB, (b+1)*RPB), each wave a contiguous run of RPW rows.  A wave finds
+// so the work is split by output rows into ranges of RPB = 4 RPW rows:
+// workgroup b copies ranges b, b + gridDim.x, ..., each wave of it a
+// contiguous run of RPW rows of the range.  A wave finds
 // the chunk of its first row (and again whenever it crosses into the next):
 //   r = number of receivers r' >= 1 with rank_offsets[r'] <= o,
 //   p = number of senders whose inclusive prefix of column r is <= o - rank_offsets[r],
@@ -791,7 +792,8 @@ __global__ __launch_bounds__(kRowThreads) void copy_splits_kernel(
 // prefix sums, a chunk reaching outside the buffers is skipped and raises
 // kErrSplits, and the workgroups take chunks in turn.  Workgroup b < W
 // also writes receiver b's row of the plan (each output may be null).
-constexpr int kA2ARowsPerWaveBytes = 16384;  // bytes a wave copies per run
+constexpr int kA2ARowsPerWaveBytes = 4096;  // bytes a wave copies per run
+constexpr int64_t kA2ABlocks = 1024;          // workgroups of one launch
 
 template <int U, bool NTL, bool NTS>
 __device__ __forceinline__ void copy_row(const u32x4* __restrict__ s, u32x4* __restrict__ d, int64_t Vr, int lane) {
