@@ -155,28 +155,29 @@ __device__ __forceinline__ u32x4 quantize16f(const float* f, float scale) {
   return u32x4{out[0], out[1], out[2], out[3]};
 }
 
-// x / scale for one row's scale, correctly rounded, with the reciprocal
-// refined once per row.  The element step is the compiler's IEEE fp32
-// divide sequence without its operand scaling: q = n r, then two corrections
-// q += (n - s q) r by fused multiply-adds.  That correction rounds correctly
-// when r is the correctly rounded 1/s (Markstein's theorem), so r is made
-// exactly that: one Newton step r0 + r0 (1 - s r0) from v_rcp_f32's result
-// (specified to 1 ulp) gives it for every scale except those whose mantissa
-// is all ones, s = 2^k (2 - 2^-23); there 1/s = 2^-k-1 (1 + 2^-24 + 2^-48 +
-// ...), just above the midpoint of 2^-k-1 and its successor, and the step
-// can stop on the midpoint and round down, so r is set to that successor
-// directly.  (Checked on the host over every mantissa and every r0 within an
-// ulp, and for the quotients at every code's rounding boundaries.)  The
-// scaling of the compiler's sequence only acts on extreme exponents, so the
-// fast form is taken for scales in [2^-60, 2^60]; there every quotient of at
-// least 2^-11 in magnitude has normal operands and exact remainders, and
-// smaller quotients give codes of zero.  The remainder is formed negated,
-// e = s q - n, and subtracted, q - e r: the same roundings (round to nearest
-// is symmetric), and a zero n keeps its sign through both corrections (with
-// e = n - s q a -0 would come back as +0).  Other scales (zero, subnormal,
-// huge, infinite, NaN) take the plain division.
+// x / scale for one row's scale, correctly rounded, from values prepared
+// once per row.  r is the correctly rounded 1/s: one Newton step
+// r0 + r0 (1 - s r0) from v_rcp_f32's result (specified to 1 ulp) gives it
+// for every scale except those whose mantissa is all ones, s = 2^k (2 -
+// 2^-23); there 1/s = 2^-k-1 (1 + 2^-24 + 2^-48 + ...), just above the
+// midpoint of 2^-k-1 and its successor, and the step can stop on the
+// midpoint and round down, so r is set to that successor directly.  Then
+// rd + rl is 1/s to about 2^-48: rd is r or the float below it, whichever
+// is not above 1/s, and rl = (1 - s rd) rd >= 0.  Per element,
+//   q0 = fma(n, rd, n rl)        within half an ulp and a little of n/s,
+//   q  = q0 - (s q0 - n) r       (two fused multiply-adds),
+// and q is the correctly rounded n/s (Markstein's theorem: the remainder of
+// a faithful quotient is exact, and one correction with the correctly
+// rounded reciprocal rounds correctly).  rl >= 0 keeps the sign of a zero n
+// through q0, and the remainder is formed negated (s q - n) and subtracted so
+// that a -0 stays -0.  (Checked on the host over every mantissa, and for the
+// quotients on and around every code's rounding boundaries.)  The fast form
+// is taken for scales in [2^-60, 2^60]; there every quotient of at least
+// 2^-11 in magnitude has normal operands and an exact remainder, and smaller
+// quotients give codes of zero.  Other scales (zero, subnormal, huge,
+// infinite, NaN) take the plain division.
 struct RowDiv {
-  float s, r;
+  float s, r, rd, rl;
   bool fast;
 };
 
@@ -189,16 +190,15 @@ __device__ __forceinline__ RowDiv row_div(float scale) {
   const uint32_t sb = __float_as_uint(d.s);
   if ((sb & 0x7fffffu) == 0x7fffffu)  // all-ones mantissa: 1/s rounds to 2^-k-1 (1 + 2^-23)
     d.r = __uint_as_float(((253u - ((sb >> 23) & 0xffu)) << 23) | 1u);
+  d.rd = __builtin_fmaf(-d.s, d.r, 1.0f) < 0.0f ? __uint_as_float(__float_as_uint(d.r) - 1u) : d.r;
+  d.rl = __builtin_fmaf(-d.s, d.rd, 1.0f) * d.rd;
   return d;
 }
 
 __device__ __forceinline__ float div_fast(float n, const RowDiv& d) {
-  float q = n * d.r;
-  float e = __builtin_fmaf(d.s, q, -n);
-  q = __builtin_fmaf(-e, d.r, q);
-  e = __builtin_fmaf(d.s, q, -n);
-  q = __builtin_fmaf(-e, d.r, q);
-  return q;
+  const float q0 = __builtin_fmaf(n, d.rd, n * d.rl);
+  const float e = __builtin_fmaf(d.s, q0, -n);
+  return __builtin_fmaf(-e, d.r, q0);
 }
 
 // Fast-path codes of 16 quotients.  fp8: gfx950's v_cvt_pk_fp8_f32 rounds

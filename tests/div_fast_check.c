@@ -9,9 +9,10 @@
  * its neighbour on the other side of 1/s).  It refines r0 once,
  *     r = fma(fma(-s, r0, 1), r0, r0),
  * except for a scale whose mantissa is all ones, s = 2^k (2 - 2^-23), where
- * r is set to 2^-k-1 (1 + 2^-23); then for every numerator n it forms
- *     q = n * r;  e = fma(s, q, -n);  q = fma(-e, r, q);
- *                 e = fma(s, q, -n);  q = fma(-e, r, q).
+ * r is set to 2^-k-1 (1 + 2^-23).  It splits 1/s as rd + rl: rd is r or the
+ * float below it, whichever is not above 1/s, and rl = fl((1 - s rd) rd).
+ * For every numerator n it forms
+ *     q0 = fma(n, rd, n * rl);  e = fma(s, q0, -n);  q = fma(-e, r, q0).
  * The fast path is only taken for 2^-60 <= s <= 2^60.
  *
  * Part 1 (every mantissa): for each of the 2^23 mantissas, at exponents
@@ -60,25 +61,40 @@ static float step_ulps(float x, int k)
     return x;
 }
 
-/* The kernel's element step.  Each step is stored through a volatile, so the host compiler cannot merge
- * a negation into a neighbouring fma (GCC rewrites -fma(a, b, -c) as
- * fnma(a, b, c), which is not exact for the sign of a zero). */
-static float div_fast(float n, float s, float r)
-{
-    volatile float q = n * r;
-    volatile float m = -n;
-    volatile float e = fmaf(s, q, m);
-    volatile float ne = -e;
-    q = fmaf(ne, r, q);
-    e = fmaf(s, q, m);
-    ne = -e;
-    q = fmaf(ne, r, q);
-    return q;
-}
-
 static uint32_t bits(float f) { uint32_t u; memcpy(&u, &f, 4); return u; }
 
 static float from_bits(uint32_t u) { float f; memcpy(&f, &u, 4); return f; }
+
+/* The kernel's element step.  Each step is stored through a volatile, so the host compiler cannot merge
+ * a negation into a neighbouring fma (GCC rewrites -fma(a, b, -c) as
+ * fnma(a, b, c), which is not exact for the sign of a zero). */
+struct row { float s, r, rd, rl; };
+
+/* The kernel's per-row values: rd is r or the float below it, whichever is
+ * not above 1/s, and rl = (1 - s rd) rd >= 0. */
+static struct row row_split(float s, float r)
+{
+    struct row w = {s, r, r, 0.0f};
+    volatile float ms = -s;
+    volatile float e0 = fmaf(ms, r, 1.0f);
+    if (e0 < 0.0f)
+        w.rd = from_bits(bits(r) - 1u);
+    volatile float e1 = fmaf(ms, w.rd, 1.0f);
+    w.rl = e1 * w.rd;
+    return w;
+}
+
+static float div_fast(float n, const struct row *w)
+{
+    volatile float lo = n * w->rl;
+    volatile float q = fmaf(n, w->rd, lo);
+    volatile float m = -n;
+    volatile float e = fmaf(w->s, q, m);
+    volatile float ne = -e;
+    q = fmaf(ne, w->r, q);
+    return q;
+}
+
 
 /* The two floats around 1/s: the correctly rounded rn and its neighbour on
  * the other side of 1/s (1 - s rn is exact in one fma; its sign tells the
@@ -106,10 +122,11 @@ static float row_recip(float s, float r0)
 
 static long long n_pairs, n_bad;
 
-static void check(float n, float s, float r, float r0)
+static void check(float n, const struct row *w, float r0)
 {
+    const float s = w->s, r = w->r;
     const float want = n / s;
-    const float got = div_fast(n, s, r);
+    const float got = div_fast(n, w);
     ++n_pairs;
     int ok;
     if (fabsf(want) >= 0x1p-11f)
@@ -194,21 +211,21 @@ int main(int argc, char **argv)
         around_recip(s, around);
         for (int k = 0; k < 2; ++k) {
             const float r0 = around[k];
-            const float r = row_recip(s, r0);
+            const struct row w = row_split(s, row_recip(s, r0));
             for (int j = 0; j < nb; ++j) {
                 const float n0 = bnd[j] * s;
                 for (int u = -NB; u <= NB; ++u) {
                     const float n = step_ulps(n0, u);
-                    check(n, s, r, r0);
-                    check(-n, s, r, r0);
+                    check(n, &w, r0);
+                    check(-n, &w, r0);
                 }
             }
             for (int j = 0; j < n_random; ++j) {
                 const float n = (float)((2.0 * uniform01() - 1.0) * 464.0) * s;
-                check(n, s, r, r0);
+                check(n, &w, r0);
             }
-            check(0.0f, s, r, r0);
-            check(-0.0f, s, r, r0);
+            check(0.0f, &w, r0);
+            check(-0.0f, &w, r0);
         }
     }
     printf("quotients %lld mismatches %lld\n", n_pairs, n_bad);
