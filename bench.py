@@ -45,12 +45,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # only, comments and whitespace aside); any other build reports traffic as
 # null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "3f2acaae9f678f1ce2bd3238d6b4ecfb01d4cebba2989e7d59287e3f3c39448d",
+    "source_sha256": "3151afd899b867872337aaeb135095d06bfbd705057de7b991da86f3e462fb86",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "1": {"ep_plan": 637548, "ep_dispatch": 235744802, "ep_combine": 236513995, "ep_dispatch_smooth": 144419496, "ep_combine_quant": 138809723, "ep_dispatch_int8": 135637233, "ep_combine_quant_int8": 138469883},
-        "2": {"ep_plan": 1921824, "ep_dispatch": 1059693272, "ep_combine": 1061201370, "ep_dispatch_smooth": 875706941, "ep_combine_quant": 600931301, "ep_dispatch_int8": 590509177, "ep_combine_quant_int8": 600623109, "ep_combine_add_rmsnorm": 1294105101, "ep_add_rmsnorm": 469938815},
-        "3": {"ep_all_to_all_splits": 268542893, "ep_plan_splits": 5920, "ep_dispatch_splits": 268605454},
-        "4": {"ep_plan": 3540153, "ep_dispatch": 885924901, "ep_combine": 1652699691, "ep_dispatch_smooth": 2301358161, "ep_combine_quant": 969623077, "ep_dispatch_int8": 885975845, "ep_combine_quant_int8": 968665477, "ep_combine_add_rmsnorm": 2118406627, "ep_add_rmsnorm": 939694403},
+        "1": {"ep_plan": 652859, "ep_dispatch": 235744315, "ep_combine": 236513975, "ep_plan_lookback": 964943, "ep_dispatch_smooth": 144419097, "ep_combine_quant": 138518557, "ep_dispatch_int8": 135555602, "ep_combine_quant_int8": 138496190},
+        "2": {"ep_plan": 1970914, "ep_dispatch": 1059610641, "ep_combine": 1061201774, "ep_plan_lookback": 2484377, "ep_dispatch_smooth": 875930400, "ep_combine_quant": 600518737, "ep_dispatch_int8": 590444061, "ep_combine_quant_int8": 600445649, "ep_combine_add_rmsnorm": 1294119284, "ep_add_rmsnorm": 469944965},
+        "3": {"ep_all_to_all_splits": 268817858, "ep_plan_splits": 5856, "ep_dispatch_splits": 268577617},
+        "4": {"ep_plan": 3606458, "ep_dispatch": 885868018, "ep_combine": 1652703665, "ep_plan_lookback": 4562074, "ep_dispatch_smooth": 2300351611, "ep_combine_quant": 968566038, "ep_dispatch_int8": 885888257, "ep_combine_quant_int8": 968237046, "ep_combine_add_rmsnorm": 2118404462, "ep_add_rmsnorm": 939700622},
     },
 }
 
