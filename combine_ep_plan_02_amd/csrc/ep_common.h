@@ -39,6 +39,23 @@ __device__ __forceinline__ uint64_t lanemask_lt() {
 
 __device__ __forceinline__ uint64_t ballot(bool p) { return __ballot(p); }
 
+// Largest of the 64 lanes' values, in every lane (all lanes active).  Within
+// each row of 16 lanes by DPP (swap neighbours, swap pairs, mirror halves of
+// 8, mirror the row: after each step a lane holds the maximum over 2, 4, 8,
+// 16 lanes), then the four rows' maxima through v_readlane.  Each step is
+// one VALU operation instead of a round trip through LDS.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xB1, 0xF, 0xF, false));   // quad_perm [1,0,3,2]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4E, 0xF, 0xF, false));   // quad_perm [2,3,0,1]
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xF, 0xF, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xF, 0xF, false));  // row_mirror
+  const uint32_t r0 = (uint32_t)__builtin_amdgcn_readlane((int)v, 0);
+  const uint32_t r1 = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t r2 = (uint32_t)__builtin_amdgcn_readlane((int)v, 32);
+  const uint32_t r3 = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(r0, r1), max(r2, r3));
+}
+
 // bf16 <-> fp32.  bf16 is the upper half of a binary32; the narrowing rounds
 // to nearest, ties to even, keeping NaNs quiet.
 __device__ __forceinline__ float bf16lo(uint32_t packed) { return __uint_as_float(packed << 16); }

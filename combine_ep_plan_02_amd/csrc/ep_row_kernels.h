@@ -297,8 +297,7 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_quant_kernel(
   }
   for (int idx = G * kRowThreads + tid; idx < NG; idx += kRowThreads)
     mbits = amax16_bits(ld<NTL>(src + 2 * idx), ld<NTL>(src + 2 * idx + 1), mbits);
-#pragma unroll
-  for (int off = kWave / 2; off > 0; off >>= 1) mbits = max(mbits, (uint32_t)__shfl_xor((int)mbits, off, kWave));
+  mbits = wave_max_u32(mbits);
   if (lane == 0) s_max[wave] = mbits;
   __syncthreads();
   uint32_t m = s_max[0];
@@ -426,7 +425,7 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_smooth_kernel(
     const u32x4* __restrict__ x, const int32_t* __restrict__ ids, const int32_t* __restrict__ pos,
     const float4* __restrict__ smooth, u32x4* __restrict__ q, float* __restrict__ scales, int T, int K,
     int E, int NG, int64_t cap_rows) {
-  __shared__ uint32_t s_max[kRowThreads / kWave];
+  __shared__ uint32_t s_max[2][kRowThreads / kWave];  // alternate copies use alternate halves
   const int t = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = lane_id();
@@ -437,16 +436,20 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_smooth_kernel(
   if (ballot(my_pos >= 0 && (unsigned)my_e >= (unsigned)E) && lane == 0) raise_device_error(kErrBadExpert);
   if (live == 0) return;
   const u32x4* src = x + (int64_t)t * NG * 2;
-  u32x4 xr[G][2];
+  // The token's values as fp32, unpacked once for all of its copies.
+  float xf[G][16];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     const int idx = g * kRowThreads + tid;
+    u32x4 a = u32x4{0, 0, 0, 0}, b = u32x4{0, 0, 0, 0};
     if (idx < NG) {
-      xr[g][0] = src[2 * idx];
-      xr[g][1] = src[2 * idx + 1];
+      a = src[2 * idx];
+      b = src[2 * idx + 1];
     }
+    unpack16(a, b, xf[g]);
   }
   uint64_t mk = live;
+  int half = 0;
   while (mk) {
     const int k = __builtin_ctzll(mk);
     mk &= mk - 1;
@@ -459,29 +462,28 @@ __global__ __launch_bounds__(kRowThreads) void dispatch_smooth_kernel(
     for (int g = 0; g < G; ++g) {
       const int idx = g * kRowThreads + tid;
       if (idx < NG) {
-        float f[16];
-        unpack16(xr[g][0], xr[g][1], f);
 #pragma unroll
         for (int qd = 0; qd < 4; ++qd) {
           const float4 sv = srow[4 * idx + qd];
-          xs[g][4 * qd + 0] = f[4 * qd + 0] * sv.x;
-          xs[g][4 * qd + 1] = f[4 * qd + 1] * sv.y;
-          xs[g][4 * qd + 2] = f[4 * qd + 2] * sv.z;
-          xs[g][4 * qd + 3] = f[4 * qd + 3] * sv.w;
+          xs[g][4 * qd + 0] = xf[g][4 * qd + 0] * sv.x;
+          xs[g][4 * qd + 1] = xf[g][4 * qd + 1] * sv.y;
+          xs[g][4 * qd + 2] = xf[g][4 * qd + 2] * sv.z;
+          xs[g][4 * qd + 3] = xf[g][4 * qd + 3] * sv.w;
         }
 #pragma unroll
         for (int j = 0; j < 16; ++j) amax = fmaxf(amax, fabsf(xs[g][j]));
       }
     }
-    uint32_t mb = __float_as_uint(amax);
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) mb = max(mb, (uint32_t)__shfl_xor((int)mb, off, kWave));
-    __syncthreads();  // the previous copy's reads of s_max are done
-    if (lane == 0) s_max[wave] = mb;
+    // Copy c's wave maxima go to half c % 2: the barrier of copy c + 1
+    // follows every wave's reads of copy c, so half c % 2 is free again
+    // when copy c + 2 writes it.
+    const uint32_t mb = wave_max_u32(__float_as_uint(amax));
+    if (lane == 0) s_max[half][wave] = mb;
     __syncthreads();
-    uint32_t m = s_max[0];
+    uint32_t m = s_max[half][0];
 #pragma unroll
-    for (int w = 1; w < kRowThreads / kWave; ++w) m = max(m, s_max[w]);
+    for (int w = 1; w < kRowThreads / kWave; ++w) m = max(m, s_max[half][w]);
+    half ^= 1;
     const float scale = __uint_as_float(m) / quant_max<QT>();
     const RowDiv rd = row_div(scale);
 #pragma unroll
