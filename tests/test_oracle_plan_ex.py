@@ -147,6 +147,40 @@ def test_dispatch_weights_gather():
     assert (ew[untouched] == -1.0).all()
 
 
+@pytest.mark.parametrize("align,pad_empty,seed", [(1, False, 0), (4, True, 1), (3, False, 2)])
+def test_dispatch_weights_brute_force_row_order(align, pad_empty, seed):
+    """expand_weights from the row order alone, without the oracle's
+    positions: expandX groups the live copies by destination rank, then
+    local expert (together: by expert id, e = d * E/W + le), then source rank,
+    then flattened (t, k) order, which for a sort key is (e, t, k) since the
+    source rank grows with t; each expert starts at the sum of the padded
+    sizes of the experts before it (PyTorch compare view
+    "ciflow/h100-symm-mem/166772", the 2-D exchange plan with major_align;
+    expandScalesOut on the CANN dispatch page carries each copy's weight to
+    its row)."""
+    rng = np.random.default_rng(70 + seed)
+    T, K, E, W = 48, 5, 12, 3
+    ids = rng.integers(0, E, size=(T, K)).astype(np.int32)
+    ids[ids == 4] = 7                                   # expert 4 left empty
+    active = (rng.random(T) < 0.75).astype(np.uint8)
+    copies = (rng.random((T, K)) < 0.85).astype(np.uint8)
+    w = (rng.random((T, K)) + 0.5).astype(np.float32)
+    live = [(int(ids[t, k]), t, k) for t in range(T) for k in range(K) if active[t] and copies[t, k]]
+    live.sort()
+    counts = [sum(1 for e, _, _ in live if e == x) for x in range(E)]
+    sizes = [((c + align - 1) // align) * align if (c or not pad_empty) else align for c in counts]
+    start = [sum(sizes[:x]) for x in range(E)]
+    cap = T * K + E * align
+    want = np.full(cap, -1.0, np.float32)
+    seen = [0] * E
+    for e, t, k in live:
+        want[start[e] + seen[e]] = w[t, k]
+        seen[e] += 1
+    p, _ = oracle.plan_ex(ids, E, W, active, copies, major_align=align, pad_empty=pad_empty)
+    got = oracle.dispatch_weights(p.pos, w, cap, fill=-1.0)
+    assert (got.view(np.uint32) == want.view(np.uint32)).all()
+
+
 @pytest.mark.parametrize("align,pad_empty", [(4, False), (16, True), (3, True)])
 def test_padding_keeps_the_true_counts(align, pad_empty):
     """Padding moves rows, not counts: in_splits, src_offsets, out_splits and
