@@ -45,12 +45,12 @@ METRIC = "dispatch+combine tokens/s and achieved HBM GB/s (% of MI355X peak), 1 
 # only, comments and whitespace aside); any other build reports traffic as
 # null until the counters are taken again.
 TRAFFIC = {
-    "source_sha256": "3151afd899b867872337aaeb135095d06bfbd705057de7b991da86f3e462fb86",
+    "source_sha256": "3e2b8e20a40b8db1ee881ece0c6f4da6b883db66a28b65a6608e02955d22aabf",
     "bytes_per_launch": {   # {workload: {phase: bytes}}
-        "1": {"ep_plan": 652859, "ep_dispatch": 235744315, "ep_combine": 236513975, "ep_plan_lookback": 964943, "ep_dispatch_smooth": 144419097, "ep_combine_quant": 138518557, "ep_dispatch_int8": 135555602, "ep_combine_quant_int8": 138496190},
-        "2": {"ep_plan": 1970914, "ep_dispatch": 1059610641, "ep_combine": 1061201774, "ep_plan_lookback": 2484377, "ep_dispatch_smooth": 875930400, "ep_combine_quant": 600518737, "ep_dispatch_int8": 590444061, "ep_combine_quant_int8": 600445649, "ep_combine_add_rmsnorm": 1294119284, "ep_add_rmsnorm": 469944965},
-        "3": {"ep_all_to_all_splits": 268817858, "ep_plan_splits": 5856, "ep_dispatch_splits": 268577617},
-        "4": {"ep_plan": 3606458, "ep_dispatch": 885868018, "ep_combine": 1652703665, "ep_plan_lookback": 4562074, "ep_dispatch_smooth": 2300351611, "ep_combine_quant": 968566038, "ep_dispatch_int8": 885888257, "ep_combine_quant_int8": 968237046, "ep_combine_add_rmsnorm": 2118404462, "ep_add_rmsnorm": 939700622},
+        "1": {"ep_plan": 652247, "ep_dispatch": 235782197, "ep_combine": 236513930, "ep_plan_lookback": 965702, "ep_dispatch_smooth": 144423938, "ep_combine_quant": 138720556, "ep_dispatch_int8": 135638980, "ep_combine_quant_int8": 138584940},
+        "2": {"ep_plan": 1961759, "ep_dispatch": 1059626988, "ep_combine": 1061201583, "ep_plan_lookback": 2485401, "ep_dispatch_smooth": 876113336, "ep_combine_quant": 600660225, "ep_dispatch_int8": 590466904, "ep_combine_quant_int8": 600736065, "ep_combine_add_rmsnorm": 1294119130, "ep_add_rmsnorm": 469944925},
+        "3": {"ep_all_to_all_splits": 268838617, "ep_plan_splits": 5856, "ep_dispatch_splits": 268576667},
+        "4": {"ep_plan": 3595139, "ep_dispatch": 885888414, "ep_combine": 1652703245, "ep_plan_lookback": 4564602, "ep_dispatch_smooth": 2301502849, "ep_combine_quant": 969073055, "ep_dispatch_int8": 885969099, "ep_combine_quant_int8": 968471102, "ep_combine_add_rmsnorm": 2118405266, "ep_add_rmsnorm": 939700448},
     },
 }
 
