@@ -269,17 +269,25 @@ def int8_encode(value: float) -> int:
 
 
 def dispatch_quant(x_bits, ids, pos, E: int, qtype: int, cap_rows: int,
-                   smooth: np.ndarray | None = None, fill_q: int = 0, fill_scale: float = 0.0):
+                   smooth: np.ndarray | None = None, fill_q: int = 0, fill_scale: float = 0.0,
+                   q: np.ndarray | None = None, scales: np.ndarray | None = None):
     """Per-copy dynamic quantisation (optionally with per-expert smoothing
-    scales [E][H] fp32).  Returns (codes [cap_rows][H] uint8, scales [cap_rows])."""
+    scales [E][H] fp32).  Returns (codes [cap_rows][H] uint8, scales [cap_rows]).
+    With `q` and `scales` given (C-contiguous, [cap_rows][H] uint8 and
+    [cap_rows] float32) the rows are written there and the rest is kept."""
     x_bits = np.ascontiguousarray(x_bits, dtype=np.uint16)
     ids = np.ascontiguousarray(ids, dtype=np.int32)
     pos = np.ascontiguousarray(pos, dtype=np.int32)
     sm = None if smooth is None else np.ascontiguousarray(smooth, dtype=np.float32)
     T, H = x_bits.shape
     K = pos.shape[1]
-    q = np.full((cap_rows, H), fill_q, np.uint8)
-    sc = np.full(cap_rows, fill_scale, np.float32)
+    if q is None:
+        q = np.full((cap_rows, H), fill_q, np.uint8)
+    if scales is None:
+        scales = np.full(cap_rows, fill_scale, np.float32)
+    assert q.shape == (cap_rows, H) and q.dtype == np.uint8 and q.flags["C_CONTIGUOUS"]
+    assert scales.shape == (cap_rows,) and scales.dtype == np.float32 and scales.flags["C_CONTIGUOUS"]
+    sc = scales
     scratch = np.zeros(H, np.float32)
     _check(_load().oracle_dispatch_quant(T, K, E, H, _ptr(x_bits), _ptr(ids), _ptr(pos), _ptr(sm),
                                          qtype, _ptr(q), _ptr(sc), cap_rows, _ptr(scratch)),

@@ -64,3 +64,44 @@ def combine(y: np.ndarray, pos: np.ndarray, weights: np.ndarray) -> np.ndarray:
 
     _run(run, T)
     return out
+
+
+def dispatch_quant(x: np.ndarray, ids: np.ndarray, pos: np.ndarray, E: int, qtype: int, cap_rows: int,
+                   smooth: np.ndarray | None, fill_q: int, fill_scale: float):
+    """Per-copy quantised rows (fp8 or int8, optionally smoothed): (codes
+    [cap_rows][H] uint8, scales [cap_rows] float32); rows no copy names hold
+    the fills."""
+    T, H = x.shape
+    q = np.full((cap_rows, H), fill_q, np.uint8)
+    sc = np.full(cap_rows, fill_scale, np.float32)
+    _run(lambda lo, hi: oracle.dispatch_quant(x[lo:hi], ids[lo:hi], pos[lo:hi], E, qtype, cap_rows,
+                                              smooth, q=q, scales=sc), T)
+    return q, sc
+
+
+def combine_quant(codes: np.ndarray, qtype: int, scales: np.ndarray, pos: np.ndarray,
+                  weights: np.ndarray) -> np.ndarray:
+    """out [T][H] uint16 from quantised expert rows, for every token."""
+    T = pos.shape[0]
+    out = np.empty((T, codes.shape[1]), np.uint16)
+
+    def run(lo, hi):
+        out[lo:hi] = oracle.combine_quant(codes, qtype, scales, pos[lo:hi], weights[lo:hi])
+
+    _run(run, T)
+    return out
+
+
+def combine_add_rmsnorm(y: np.ndarray, pos: np.ndarray, weights: np.ndarray, residual: np.ndarray,
+                        gamma: np.ndarray, eps: float):
+    """(residual_out, norm_out) [T][H] uint16 each, for every token."""
+    T = pos.shape[0]
+    ro = np.empty((T, y.shape[1]), np.uint16)
+    no = np.empty((T, y.shape[1]), np.uint16)
+
+    def run(lo, hi):
+        ro[lo:hi], no[lo:hi] = oracle.combine_add_rmsnorm(y, pos[lo:hi], weights[lo:hi], residual[lo:hi],
+                                                          gamma, eps)
+
+    _run(run, T)
+    return ro, no
