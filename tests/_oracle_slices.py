@@ -17,7 +17,7 @@ import oracle
 
 
 def host_threads() -> int:
-    """Host threads for the oracle (at most 16, the CPU share of a one-GPU machine)."""
+    """Host threads for the oracle: the CPUs this process may run on, at most 16."""
     try:
         n = len(os.sched_getaffinity(0))
     except AttributeError:
