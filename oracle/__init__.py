@@ -22,6 +22,9 @@ import numpy as np
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "ep_oracle.c")
 _LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# A compiled oracle to load instead of liboracle.so (not rebuilt); the
+# mutation test points it at builds of ep_oracle.c with one planted mistake.
+_LIB_OVERRIDE = os.environ.get("EP_ORACLE_LIB")
 
 DEVERR_BAD_EXPERT = 1
 DEVERR_SPLITS = 2
@@ -47,9 +50,12 @@ def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
-        build()
-    lib = ctypes.CDLL(_LIB_PATH)
+    if _LIB_OVERRIDE:
+        lib = ctypes.CDLL(_LIB_OVERRIDE)
+    else:
+        if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+            build()
+        lib = ctypes.CDLL(_LIB_PATH)
     P = ctypes.c_void_p
     i32, i64 = ctypes.c_int32, ctypes.c_int64
     lib.oracle_bf16_to_f32.argtypes = [ctypes.c_uint16]
